@@ -1,0 +1,203 @@
+"""Workload descriptions and seeded synthetic inputs.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+draws random numbers and converts them to bfloat16; it holds none of the
+attention, RoPE, KV-cache or projection arithmetic (that lives in the HIP
+library and, independently, in the CPU oracle).
+
+Workload shapes follow the UnStep paper (arXiv 2609.32518): an 81-frame
+832x480 clip whose initial latent noise is 1x21x16x60x104 (appendix Table 3),
+generated as seven causal chunks of three latent frames each (Table 3), by a
+Wan2.1-1.3B DiT (Table 1 caption).  With a 1x2x2 patch a latent frame is
+30x52 = 1560 tokens; the DiT has hidden size 1536 = 12 heads x 128.  The
+window sizes (3 sink + 6 recent frames, 3 sink + 9 recent at 720p) and the
+SVD ranks (512, 256, 16) are workload parameters the paper leaves open; they
+are fixed here per workload.
+
+Seeds: every tensor is drawn from PCG64 seeded with
+``SeedSequence([0, workload_id, tag, chunk, step, layer])``.  Floating values
+are drawn in float32 and rounded to bfloat16 with round-to-nearest-even, and
+are stored as uint16 bit patterns so that both the oracle (which widens them
+exactly to float64) and the GPU see the very same values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+# tensor tags for the seed sequence
+TAG_X = 1
+TAG_Q = 2
+TAG_K = 3
+TAG_V = 4
+TAG_WQ = 5
+TAG_WK = 6
+TAG_WV = 7
+TAG_WO = 8
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One workload: the geometry of a DiT self-attention layer and its cache."""
+
+    wid: int                 # workload id, part of every seed
+    name: str
+    grid_h: int              # latent-frame token grid
+    grid_w: int
+    n_heads: int
+    head_dim: int
+    pairs: Tuple[int, int, int]   # RoPE pairs on the (frame, row, col) axes
+    theta: float
+    chunk_frames: int        # latent frames per causal chunk
+    n_chunks: int            # chunks appended in order
+    n_slots: int             # frame slots in the KV ring
+    n_sink: int              # leading frames pinned in the ring
+    n_recent: int            # recent prior frames in the window, -1 = all
+    rank: Optional[int]      # SVD rank of the V/O projections, None = dense
+    n_tab_frames: int        # frames covered by the RoPE table
+    layers: int = 1
+    first_steps: int = 1     # denoising forwards of the first chunk
+    later_steps: int = 1     # denoising forwards of every later chunk
+    clean_pass: bool = False # one extra clean-cache forward per chunk
+    x_std: float = 1.0
+
+    @property
+    def T(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def hidden(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def n_q(self) -> int:
+        return self.chunk_frames * self.T
+
+    @property
+    def w_std(self) -> float:
+        return 1.0 / np.sqrt(self.hidden)
+
+    def geom_tuple(self):
+        return (self.grid_h, self.grid_w, self.n_heads, self.head_dim,
+                self.pairs[0], self.pairs[1], self.pairs[2], self.chunk_frames)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+TINY = Workload(wid=0, name="tiny", grid_h=4, grid_w=6, n_heads=1, head_dim=64,
+                pairs=(12, 10, 10), theta=10000.0, chunk_frames=3, n_chunks=3,
+                n_slots=9, n_sink=1, n_recent=3, rank=16, n_tab_frames=9)
+# same as TINY but with the smallest ring that holds the window, so slots wrap
+TINY_WRAP = TINY.replace(name="tiny_wrap", n_slots=7)
+
+WAN_FULL = Workload(wid=1, name="wan_full", grid_h=30, grid_w=52, n_heads=12,
+                    head_dim=128, pairs=(22, 21, 21), theta=10000.0,
+                    chunk_frames=3, n_chunks=7, n_slots=21, n_sink=0,
+                    n_recent=-1, rank=None, n_tab_frames=21)
+
+WAN_WINDOW = Workload(wid=2, name="wan_window", grid_h=30, grid_w=52, n_heads=12,
+                      head_dim=128, pairs=(22, 21, 21), theta=10000.0,
+                      chunk_frames=3, n_chunks=6, n_slots=21, n_sink=3,
+                      n_recent=6, rank=512, n_tab_frames=21)
+
+WAN_CLIP = Workload(wid=3, name="wan_clip", grid_h=30, grid_w=52, n_heads=12,
+                    head_dim=128, pairs=(22, 21, 21), theta=10000.0,
+                    chunk_frames=3, n_chunks=7, n_slots=21, n_sink=3,
+                    n_recent=6, rank=512, n_tab_frames=21, layers=30,
+                    first_steps=4, later_steps=2, clean_pass=True)
+
+WAN_720P = Workload(wid=4, name="wan_720p", grid_h=45, grid_w=80, n_heads=12,
+                    head_dim=128, pairs=(22, 21, 21), theta=10000.0,
+                    chunk_frames=3, n_chunks=7, n_slots=15, n_sink=3,
+                    n_recent=9, rank=256, n_tab_frames=21)
+
+ALL = {w.name: w for w in (TINY, TINY_WRAP, WAN_FULL, WAN_WINDOW, WAN_CLIP, WAN_720P)}
+
+
+# ---------------------------------------------------------------- bf16 bits
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) exactly to float64."""
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- draws
+
+def rng(w: Workload, tag: int, chunk: int = 0, step: int = 0, layer: int = 0):
+    ss = np.random.SeedSequence([0, w.wid, tag, chunk, step, layer])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def normal_bf16(w: Workload, shape, tag, chunk=0, step=0, layer=0, std=1.0):
+    """N(0, std^2) drawn in float32, rounded to bf16; returns uint16 bits."""
+    g = rng(w, tag, chunk, step, layer)
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x = (x.astype(np.float64) * std).astype(np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def chunk_tokens(w: Workload, tag: int, chunk: int, step: int = 0, layer: int = 0):
+    """A chunk's per-token head vectors, [chunk_frames*T][H][D] bf16 bits.
+
+    Token n of the chunk is latent frame chunk*C + n // T, position
+    (y, x) = divmod(n % T, grid_w) in that frame."""
+    return normal_bf16(w, (w.n_q, w.n_heads, w.head_dim), tag, chunk, step, layer)
+
+
+def activations(w: Workload, chunk: int, step: int = 0):
+    """Hidden states X of one chunk forward, [chunk_frames*T][hidden] bf16."""
+    return normal_bf16(w, (w.n_q, w.hidden), TAG_X, chunk, step, 0, std=w.x_std)
+
+
+def dense_weight_f64(w: Workload, tag: int, layer: int = 0) -> np.ndarray:
+    """A random projection matrix W ~ N(0, 1/hidden), applied as X @ W, in fp64."""
+    g = rng(w, tag, 0, 0, layer)
+    return g.standard_normal(size=(w.hidden, w.hidden)) * w.w_std
+
+
+def dense_weight_bf16(w: Workload, tag: int, layer: int = 0):
+    """W rounded to bf16, [in][out] bits."""
+    return f32_to_bf16_bits(dense_weight_f64(w, tag, layer).astype(np.float32))
+
+
+def svd_factors_f64(w: Workload, tag: int, rank: int, layer: int = 0):
+    """Rank-r factors of a random projection W (in x out, fp64).
+
+    W = U S V^T; A = U[:, :r] sqrt(S_r)  (in x r), B = sqrt(S_r) V[:, :r]^T
+    (r x out).  This is the offline weight preparation of the truncated-SVD
+    projections (UnStep, abstract); it is input data for the projection step,
+    not part of it.  Returns (A, B) in fp64."""
+    W = dense_weight_f64(w, tag, layer)
+    U, S, Vt = np.linalg.svd(W)
+    rs = np.sqrt(S[:rank])
+    return U[:, :rank] * rs[None, :], rs[:, None] * Vt[:rank, :]
+
+
+def svd_factors_bf16(w: Workload, tag: int, rank: int, layer: int = 0):
+    """svd_factors_f64 rounded to bf16: (A bits [in][r], B bits [r][out])."""
+    A, B = svd_factors_f64(w, tag, rank, layer)
+    return (f32_to_bf16_bits(A.astype(np.float32)),
+            f32_to_bf16_bits(B.astype(np.float32)))

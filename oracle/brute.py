@@ -1,0 +1,111 @@
+"""Brute-force scalar versions of the oracle's steps, for tiny inputs only.
+
+TEST INFRASTRUCTURE ONLY.  Pure-Python loops over the definitions, written by
+a different route from ust_oracle (complex multiplication for RoPE, a frame
+membership test per key for the window, scalar sums for the products), so a
+slip in either shows up as a mismatch.  Citations as in ust_oracle.
+"""
+from __future__ import annotations
+
+import cmath
+import math
+from typing import List, Sequence
+
+
+def rope_rotate(vec: Sequence[float], f: int, y: int, x: int,
+                pairs: Sequence[int], theta: float) -> List[float]:
+    """RoPE of one head vector as complex multiplication: the pair
+    (v[2p], v[2p+1]) is the complex number v[2p] + i v[2p+1], multiplied by
+    exp(i * pos * theta**(-j/n)) for pair j of its axis (UnStep, abstract:
+    3-D RoPE with cached coefficients; axis split is a reading)."""
+    out = []
+    p = 0
+    for axis_pairs, pos in zip(pairs, (f, y, x)):
+        for j in range(axis_pairs):
+            z = complex(vec[2 * p], vec[2 * p + 1])
+            w = z * cmath.exp(1j * pos * math.pow(theta, -j / axis_pairs))
+            out.extend([w.real, w.imag])
+            p += 1
+    return out
+
+
+def in_window(frame: int, frame_start: int, chunk_frames: int, n_sink: int,
+              n_recent: int) -> bool:
+    """Is latent frame `frame` visible to the chunk starting at frame_start?"""
+    if frame_start <= frame < frame_start + chunk_frames:
+        return True
+    if frame >= frame_start:
+        return False
+    if frame < n_sink:
+        return True
+    return n_recent < 0 or frame_start - frame <= n_recent
+
+
+def ring_simulation(n_frames: int, n_slots: int, n_sink: int) -> List[int]:
+    """Slot of each frame 0..n_frames-1 found by simulating the cache: sinks
+    take the next free slot for good; every other frame takes a free slot if
+    one is left, else the slot of the oldest non-sink frame still held."""
+    held = {}                      # slot -> frame
+    order = []                     # non-sink slots, oldest first
+    out = []
+    for f in range(n_frames):
+        free = [s for s in range(n_slots) if s not in held]
+        if f < n_sink:
+            s = free[0]
+        elif free:
+            s = free[0]
+            order.append(s)
+        else:
+            s = order.pop(0)
+            order.append(s)
+        held[s] = f
+        out.append(s)
+    return out
+
+
+def attention(q_rows, keys, values, scale):
+    """Softmax attention for lists of vectors: returns (outputs, lse)."""
+    outs, lses = [], []
+    for qv in q_rows:
+        scores = [scale * sum(a * b for a, b in zip(qv, kv)) for kv in keys]
+        m = max(scores)
+        ex = [math.exp(s - m) for s in scores]
+        tot = sum(ex)
+        o = [sum(e * vv[d] for e, vv in zip(ex, values)) / tot
+             for d in range(len(values[0]))]
+        outs.append(o)
+        lses.append(m + math.log(tot))
+    return outs, lses
+
+
+def window_attention(q, k_chunks, v_chunks, frame_start, chunk_frames,
+                     grid_h, grid_w, n_sink, n_recent, pairs, theta, head):
+    """Attention of a chunk's queries (un-rotated, [n][H][D] nested lists) for
+    one head over every key of every frame so far that lies in the window.
+
+    k_chunks / v_chunks: {frame: [T][H][D]} un-rotated keys and values of all
+    frames written so far.  Keys are rotated here, at their own position."""
+    T = grid_h * grid_w
+    D = len(q[0][head])
+    keys, values = [], []
+    for f in sorted(k_chunks):
+        if not in_window(f, frame_start, chunk_frames, n_sink, n_recent):
+            continue
+        for t in range(T):
+            keys.append(rope_rotate(k_chunks[f][t][head], f, t // grid_w,
+                                    t % grid_w, pairs, theta))
+            values.append(list(v_chunks[f][t][head]))
+    q_rows = []
+    for n in range(len(q)):
+        f = frame_start + n // T
+        t = n % T
+        q_rows.append(rope_rotate(q[n][head], f, t // grid_w, t % grid_w,
+                                  pairs, theta))
+    return attention(q_rows, keys, values, 1.0 / math.sqrt(D))
+
+
+def matmul(a, b):
+    """Plain triple loop over nested lists."""
+    n, k, m = len(a), len(b), len(b[0])
+    return [[sum(a[i][t] * b[t][j] for t in range(k)) for j in range(m)]
+            for i in range(n)]
