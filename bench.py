@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the windowed chunk-attention hot path on one MI355X.
+
+A step is one layer-chunk of the path at the Wan2.1-1.3B windowed workload,
+steady state (chunk 5: frames 15-17; window = 3 sink + 6 recent + 3 current
+frames = 18720 keys; 4680 queries; 12 heads x 128; rank-512 V/O):
+    V = (X A_v) B_v  ->  RoPE-K + KV append  ->  window plan + RoPE-Q +
+    windowed attention  ->  Y = (O A_o) B_o
+with every input resident in HBM when the timed region starts (the ring holds
+the window's earlier frames, written by the same path before timing).
+
+Prints one JSON line.  `value` is the attention's algorithmic TFLOP per
+layer-chunk divided by the whole step's time; `roofline` is the attention
+kernel's own rate, timed with HIP events on its stream inside the timed
+region; `cpu_baseline` is the CPU fp64 oracle on a bounded sample of the same
+layer-chunk.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
+          "% MFMA/HBM peak")
+
+# HBM traffic of one attention launch from rocprofv3 --pmc (FETCH_SIZE and
+# WRITE_SIZE per dispatch, scaled by the counter-to-byte factor of a copy of
+# known size); None until measured for the current kernel.
+ATTN_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1560,
+                    help="query rows of the oracle's sample (of 4680)")
+    return ap.parse_args()
+
+
+def attn_flops(n_q, n_k, d, h):
+    return 4.0 * n_q * n_k * d * h      # QK^T and PV, 2 flop per multiply-add
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU runs are not part of it", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_video_diffusion_amd as cvd
+    from causal_video_diffusion_amd import _binding as B
+    from causal_video_diffusion_amd import path as P
+    from causal_video_diffusion_amd import workload as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load()
+    torch.cuda.set_device(0)
+    w = wl.WAN_WINDOW
+    C = 5                                   # steady-state chunk
+    F0 = 3 * C
+    g = cvd.geom(*w.geom_tuple())
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs, resident in HBM ----
+    av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
+    ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, w.rank)
+    wv, wo = P.LowRank.from_bits(av, bv), P.LowRank.from_bits(ao, bo)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=0x7FC1)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank)
+    chunks = []
+    for c in range(C + 1):
+        chunks.append((P.to_device_bf16(wl.activations(w, c)),
+                       P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_Q, c).reshape(w.n_q, -1)),
+                       P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_K, c).reshape(w.n_q, -1))))
+    for c in range(C):                      # fill the window's earlier frames
+        x, q, k = chunks[c]
+        P.layer_chunk(g, ring, table, x, q, k, wv, wo, 3 * c, w.n_recent, bufs)
+    torch.cuda.synchronize()
+    x, q, k = chunks[C]
+    frames, _ = B.ust_window_plan(g, ring.abi, F0, w.n_recent)
+    n_k = len(frames) * w.T
+    flops = attn_flops(w.n_q, n_k, w.head_dim, w.n_heads)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        P.lowrank_apply(wv, x, bufs.v, bufs.t_v)
+        if ev is not None:
+            ev[1].record(stream)
+        B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
+        if ev is not None:
+            ev[2].record(stream)
+        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
+                          w.n_recent, 0.0, bufs.o, None)
+        if ev is not None:
+            ev[3].record(stream)
+        P.lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    names = ["v_proj_us", "rope_k_append_us", "window_attn_us", "o_proj_us"]
+    stage = {n: 1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+             for i, n in enumerate(names)}
+    attn_us = stage["window_attn_us"]
+    attn_tflops = flops / (attn_us * 1e-6) / 1e12
+    append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
+    lowrank_flops = 2 * 2.0 * w.n_q * w.hidden * w.rank
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "wan_window layer-chunk: Wan2.1-1.3B self-attention layer, "
+                        "12 heads x 128, 30x52 = 1560 tokens/frame, 3-frame chunk = 4680 "
+                        "queries, window 3 sink + 6 recent + 3 current frames = 18720 keys, "
+                        "21-slot ring, rank-512 V/O, steady-state chunk 5",
+            "n_q": w.n_q, "n_k": n_k, "n_heads": w.n_heads, "head_dim": w.head_dim,
+            "rank": w.rank, "attn_gflop": round(flops / 1e9, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": ATTN_TRAFFIC_BYTES,
+            "kernel": "window_attn_kernel<128>",
+            "kernel_us": round(attn_us, 2),
+        },
+        "stages_us": {k: round(v, 2) for k, v in stage.items()},
+        "stages": {
+            "rope_k_append_GBs": round(append_bytes / (stage["rope_k_append_us"] * 1e-6) / 1e9, 1),
+            "rope_k_append_hbm_frac": round(append_bytes / (stage["rope_k_append_us"] * 1e-6)
+                                            / 1e9 / PEAK_HBM_GBS, 4),
+            "lowrank_v_o_TFLOPs": round(lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"])
+                                                         * 1e-6) / 1e12, 1),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, C, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, C, rows_n):
+    """The CPU fp64 oracle, untuned, on a bounded sample of the same
+    layer-chunk: the V projection, the chunk's KV append and the windowed
+    attention for `rows_n` query rows (the full window for each)."""
+    import numpy as np
+    import oracle as O
+    from causal_video_diffusion_amd import workload as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    f64 = wl.bf16_bits_to_f64
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
+    # window frames of the earlier chunks (setup, not timed)
+    for c in range(C):
+        O.kv_append(cache, f64(wl.chunk_tokens(w, wl.TAG_K, c)),
+                    f64(wl.chunk_tokens(w, wl.TAG_V, c)), cos, sin, 3 * c, 3,
+                    w.grid_h, w.grid_w, w.n_slots, w.n_sink)
+    xb = f64(wl.activations(w, C))
+    kb = f64(wl.chunk_tokens(w, wl.TAG_K, C))
+    qb = f64(wl.chunk_tokens(w, wl.TAG_Q, C))
+    rows = np.arange(rows_n)
+    t0 = time.perf_counter()
+    v = O.lowrank_proj(xb, f64(av), f64(bv)).reshape(w.n_q, w.n_heads, -1)
+    O.kv_append(cache, kb, v, cos, sin, 3 * C, 3, w.grid_h, w.grid_w, w.n_slots, w.n_sink)
+    O.window_attn(cache, qb, cos, sin, 3 * C, 3, w.grid_h, w.grid_w, w.n_slots, w.n_sink,
+                  w.n_recent, rows=rows)
+    dt = time.perf_counter() - t0
+    frames = O.window_frames(3 * C, 3, w.n_sink, w.n_recent)
+    flops = attn_flops(rows_n, len(frames) * w.T, w.head_dim, w.n_heads)
+    return {
+        "value": round(flops / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": f"one wan_window steady-state layer-chunk, {rows_n} of {w.n_q} query rows: "
+                  f"full V projection + KV append of the chunk, then fp64 attention of the "
+                  f"sampled rows over all {len(frames) * w.T} window keys (materialised "
+                  f"softmax); value = sampled attention flops / wall time; BLAS threads = "
+                  f"cores, NumPy elementwise work single-threaded",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,108 @@
+// RoPE the chunk's keys and append keys and values to the frame-slot ring
+// (UnStep, abstract: KV cache indexed by latent frame, fused RoPE with cached
+// coefficients).
+//
+// One workgroup handles 64 tokens of one latent frame for one head:
+//   keys:   16-byte loads of k_new and of the table's cos/sin for four
+//           rotation pairs, rotation in fp32, bf16 rounding, 16-byte stores
+//           into the key slot [slot][h][t][:]  (a straight row copy);
+//   values: 16-byte loads into an LDS tile [token][dim], then 16-byte stores
+//           of 8 consecutive tokens per dimension into the transposed value
+//           slot [slot][h][dim][t] (the layout the attention's PV product
+//           reads without a transpose).
+// The work is a streaming copy with no reuse (HBM-bound); the table rows are
+// re-read by every head from L2.
+
+#include "ust_device.h"
+#include "ust_internal.h"
+
+namespace ust {
+namespace {
+
+constexpr int kTok = 64;  // tokens per workgroup
+
+template <int D>
+__global__ void __launch_bounds__(256)
+kv_append_kernel(AppendArgs a) {
+  constexpr int P = D / 2;
+  constexpr int CH = D / 8;          // 16-byte chunks per head row
+  constexpr int LROW = D / 2 + 1;    // LDS row stride in dwords (padded)
+  __shared__ uint32_t vt[kTok * LROW];
+
+  const int ntile = (a.T + kTok - 1) / kTok;
+  const int fi = blockIdx.x / ntile;             // frame within the chunk
+  const int t0 = (blockIdx.x % ntile) * kTok;    // first token of the tile
+  const int nt = min(kTok, a.T - t0);            // tokens here, a multiple of 8
+  const int h = blockIdx.y;
+  const int slot = a.chunk_slot[fi];
+  const int64_t row0 = int64_t(fi) * a.T + t0;   // chunk token index of t0
+  const int64_t tab0 = (int64_t(a.frame_start) * a.T + row0) * P;
+
+  uint16_t* kdst = a.k_cache + ((int64_t(slot) * a.H + h) * a.T + t0) * D;
+
+#pragma unroll
+  for (int it = 0; it < (kTok * CH) / 256; ++it) {
+    const int c = threadIdx.x + 256 * it;
+    const int tl = c / CH;
+    const int dc = c % CH;
+    if (tl < nt) {
+      const int64_t src = ((row0 + tl) * a.H + h) * D + dc * 8;
+      const uint4 kw = *reinterpret_cast<const uint4*>(a.k_new + src);
+      const uint4 vw = *reinterpret_cast<const uint4*>(a.v_new + src);
+      const float4 cs = *reinterpret_cast<const float4*>(a.cos_tab + tab0 + int64_t(tl) * P + dc * 4);
+      const float4 sn = *reinterpret_cast<const float4*>(a.sin_tab + tab0 + int64_t(tl) * P + dc * 4);
+      const uint32_t kin[4] = {kw.x, kw.y, kw.z, kw.w};
+      const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
+      const float s4[4] = {sn.x, sn.y, sn.z, sn.w};
+      uint32_t kout[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo(kin[e]);
+        const float x1 = bf16_hi(kin[e]);
+        kout[e] = pack_bf16x2(x0 * c4[e] - x1 * s4[e], x0 * s4[e] + x1 * c4[e]);
+      }
+      *reinterpret_cast<uint4*>(kdst + int64_t(tl) * D + dc * 8) =
+          make_uint4(kout[0], kout[1], kout[2], kout[3]);
+      uint32_t* row = vt + tl * LROW + dc * 4;
+      row[0] = vw.x;
+      row[1] = vw.y;
+      row[2] = vw.z;
+      row[3] = vw.w;
+    }
+  }
+  __syncthreads();
+
+  // transposed values: item = (dim d, group of 8 tokens)
+  uint16_t* vdst = a.v_cache + (int64_t(slot) * a.H + h) * D * a.TV + t0;
+  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+#pragma unroll
+  for (int it = 0; it < (D * (kTok / 8)) / 256; ++it) {
+    const int c = threadIdx.x + 256 * it;
+    const int tg = c % (kTok / 8);
+    const int d = c / (kTok / 8);
+    if (tg * 8 < nt) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = vt16[(tg * 8 + 2 * e) * (2 * LROW) + d];
+        const uint32_t hi = vt16[(tg * 8 + 2 * e + 1) * (2 * LROW) + d];
+        w[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(vdst + int64_t(d) * a.TV + tg * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
+  const int ntile = (a.T + kTok - 1) / kTok;
+  dim3 grid(ntile * a.C, a.H);
+  if (a.D == 128)
+    hipLaunchKernelGGL(kv_append_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ust

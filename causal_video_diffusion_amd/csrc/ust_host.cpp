@@ -1,0 +1,316 @@
+// C-ABI entry points: argument validation, the frame-slot ring and the
+// window plan (host integer work), and dispatch to the kernel launchers.
+//
+// Every entry point validates everything before launching anything, records
+// a thread-local error text, and never lets a C++ exception escape.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "ust_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ust_status fail(ust_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ust_status ok() {
+  g_last_error.clear();
+  return UST_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ust_status check_geom(const ust_geom* g) {
+  if (!g) return fail(UST_E_NULL, "geometry is NULL");
+  if (g->grid_h <= 0 || g->grid_w <= 0 || g->n_heads <= 0 || g->head_dim <= 0 ||
+      g->chunk_frames <= 0 || g->pairs_t < 0 || g->pairs_h < 0 || g->pairs_w < 0)
+    return fail(UST_E_SHAPE, "geometry sizes must be positive");
+  if (g->head_dim % 2 != 0 || g->pairs_t + g->pairs_h + g->pairs_w != g->head_dim / 2)
+    return fail(UST_E_SHAPE, "pairs_t+pairs_h+pairs_w (%d) must equal head_dim/2 (%d)",
+                g->pairs_t + g->pairs_h + g->pairs_w, g->head_dim / 2);
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(UST_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", g->head_dim);
+  if (g->chunk_frames > 8)
+    return fail(UST_E_UNSUPPORTED, "chunk_frames %d: at most 8 supported", g->chunk_frames);
+  const int64_t T = int64_t(g->grid_h) * g->grid_w;
+  const int64_t nq = T * g->chunk_frames;
+  if (nq * g->n_heads * g->head_dim >= (int64_t(1) << 31))
+    return fail(UST_E_SHAPE, "chunk tensor too large for 32-bit indexing");
+  return UST_OK;
+}
+
+// Slot of a frame; -1 on invalid input.
+int32_t slot_of(int32_t frame, int32_t n_slots, int32_t n_sink) {
+  if (frame < 0 || n_sink < 0 || n_slots <= n_sink) return -1;
+  if (frame < n_sink) return frame;
+  return n_sink + (frame - n_sink) % (n_slots - n_sink);
+}
+
+ust_status check_kv(const ust_kv* kv) {
+  if (!kv) return fail(UST_E_NULL, "kv is NULL");
+  if (!kv->k || !kv->v) return fail(UST_E_NULL, "kv.k or kv.v is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(UST_E_ALIGN, "kv.k / kv.v must be 16-byte aligned");
+  if (kv->n_sink < 0 || kv->n_slots <= kv->n_sink)
+    return fail(UST_E_RANGE, "ring needs 0 <= n_sink < n_slots (got %d, %d)", kv->n_sink,
+                kv->n_slots);
+  return UST_OK;
+}
+
+// Slots of the chunk's own frames; they must be distinct and the frames must
+// lie in the table.
+ust_status chunk_slots(const ust_geom* g, const ust_kv* kv, int32_t n_tab_frames,
+                       int32_t frame_start, int32_t* slots) {
+  if (frame_start < 0) return fail(UST_E_RANGE, "frame_start %d < 0", frame_start);
+  if (int64_t(frame_start) + g->chunk_frames > n_tab_frames)
+    return fail(UST_E_RANGE, "frames %d..%d outside the RoPE table of %d frames", frame_start,
+                frame_start + g->chunk_frames - 1, n_tab_frames);
+  for (int i = 0; i < g->chunk_frames; ++i) {
+    slots[i] = slot_of(frame_start + i, kv->n_slots, kv->n_sink);
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i])
+        return fail(UST_E_RANGE, "ring of %d slots (%d sinks) cannot hold one chunk of %d frames",
+                    kv->n_slots, kv->n_sink, g->chunk_frames);
+  }
+  return UST_OK;
+}
+
+// The window plan (see ust_window_plan in ust.h).
+ust_status plan(const ust_geom* g, const ust_kv* kv, int32_t frame_start, int32_t n_recent,
+                int32_t* frames, int32_t* slots, int32_t cap, int32_t* n_out) {
+  if (frame_start < 0) return fail(UST_E_RANGE, "frame_start %d < 0", frame_start);
+  if (n_recent < -1) return fail(UST_E_RANGE, "n_recent %d < -1", n_recent);
+  const int32_t last = frame_start + g->chunk_frames - 1;  // newest frame written
+  const int32_t ring = kv->n_slots - kv->n_sink;
+  int32_t n = 0;
+  for (int32_t f = 0; f <= last; ++f) {
+    const bool current = f >= frame_start;
+    const bool sink = f < kv->n_sink;
+    const bool recent = n_recent < 0 || f >= frame_start - n_recent;
+    if (!(current || sink || recent)) continue;
+    // a ring frame f is overwritten once frame f + ring has been written
+    if (!sink && int64_t(f) + ring <= last)
+      return fail(UST_E_RANGE,
+                  "window frame %d is no longer in the ring (%d slots, %d sinks) after frame %d",
+                  f, kv->n_slots, kv->n_sink, last);
+    if (n >= UST_MAX_WINDOW_FRAMES)
+      return fail(UST_E_RANGE, "window exceeds %d frames", UST_MAX_WINDOW_FRAMES);
+    if (n >= cap) return fail(UST_E_SHAPE, "plan capacity %d too small", cap);
+    frames[n] = f;
+    slots[n] = slot_of(f, kv->n_slots, kv->n_sink);
+    ++n;
+  }
+  *n_out = n;
+  return UST_OK;
+}
+
+ust_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(UST_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ust_v_row_len(int32_t T) {
+  if (T <= 0) return -1;
+  return (T + 63) / 64 * 64;
+}
+
+const char* ust_status_str(ust_status s) {
+  switch (s) {
+    case UST_OK: return "UST_OK";
+    case UST_E_NULL: return "UST_E_NULL";
+    case UST_E_SHAPE: return "UST_E_SHAPE";
+    case UST_E_RANGE: return "UST_E_RANGE";
+    case UST_E_ALIGN: return "UST_E_ALIGN";
+    case UST_E_UNSUPPORTED: return "UST_E_UNSUPPORTED";
+    case UST_E_HIP: return "UST_E_HIP";
+  }
+  return "UST_E_UNKNOWN";
+}
+
+const char* ust_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ust_slot_of_frame(const ust_kv* kv, int32_t frame) {
+  if (!kv) return -1;
+  return slot_of(frame, kv->n_slots, kv->n_sink);
+}
+
+ust_status ust_window_plan(const ust_geom* g, const ust_kv* kv, int32_t frame_start,
+                           int32_t n_recent, int32_t* frames_out, int32_t* slots_out,
+                           int32_t cap, int32_t* n_out) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    if (!kv) return fail(UST_E_NULL, "kv is NULL");
+    if (kv->n_sink < 0 || kv->n_slots <= kv->n_sink)
+      return fail(UST_E_RANGE, "ring needs 0 <= n_sink < n_slots");
+    if (!frames_out || !slots_out || !n_out) return fail(UST_E_NULL, "output pointer is NULL");
+    s = plan(g, kv, frame_start, n_recent, frames_out, slots_out, cap, n_out);
+    if (s != UST_OK) return s;
+    return ok();
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double theta,
+                                float* cos_out, float* sin_out, hipStream_t stream) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    if (!cos_out || !sin_out) return fail(UST_E_NULL, "cos_out / sin_out is NULL");
+    if (!aligned16(cos_out) || !aligned16(sin_out))
+      return fail(UST_E_ALIGN, "table pointers must be 16-byte aligned");
+    if (n_frames <= 0) return fail(UST_E_SHAPE, "n_frames %d <= 0", n_frames);
+    if (!(theta > 0.0) || !std::isfinite(theta)) return fail(UST_E_RANGE, "theta must be > 0");
+    if (int64_t(n_frames) * g->grid_h * g->grid_w * (g->head_dim / 2) >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "table too large for 32-bit indexing");
+    ust::RopeTableArgs a{cos_out, sin_out, n_frames, g->grid_h, g->grid_w,
+                         g->pairs_t, g->pairs_h, g->pairs_w, theta};
+    return hip_status(ust::launch_rope_table(a, stream), "rope_table launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
+                         const void* v_new, const float* cos_tab, const float* sin_tab,
+                         int32_t n_tab_frames, int32_t frame_start, hipStream_t stream) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    s = check_kv(kv);
+    if (s != UST_OK) return s;
+    if (!k_new || !v_new || !cos_tab || !sin_tab)
+      return fail(UST_E_NULL, "k_new, v_new or table pointer is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_tab) || !aligned16(sin_tab))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    const int32_t T = g->grid_h * g->grid_w;
+    if (T % 8 != 0)
+      return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
+    ust::AppendArgs a{};
+    s = chunk_slots(g, kv, n_tab_frames, frame_start, a.chunk_slot);
+    if (s != UST_OK) return s;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.cos_tab = cos_tab;
+    a.sin_tab = sin_tab;
+    a.k_cache = static_cast<uint16_t*>(kv->k);
+    a.v_cache = static_cast<uint16_t*>(kv->v);
+    a.T = T;
+    a.TV = ust_v_row_len(T);
+    a.H = g->n_heads;
+    a.D = g->head_dim;
+    a.C = g->chunk_frames;
+    a.frame_start = frame_start;
+    return hip_status(ust::launch_kv_append(a, stream), "kv_append launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
+                           const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
+                           int32_t frame_start, int32_t n_recent, float scale, void* out,
+                           float* lse_opt, hipStream_t stream) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    s = check_kv(kv);
+    if (s != UST_OK) return s;
+    if (!q || !cos_tab || !sin_tab || !out)
+      return fail(UST_E_NULL, "q, table or out pointer is NULL");
+    if (!aligned16(q) || !aligned16(cos_tab) || !aligned16(sin_tab) || !aligned16(out) ||
+        (lse_opt && !aligned16(lse_opt)))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    const int32_t T = g->grid_h * g->grid_w;
+    if (T % 8 != 0)
+      return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
+    if (!std::isfinite(scale) || scale < 0.f) return fail(UST_E_RANGE, "scale must be >= 0");
+    int32_t cslots[8];
+    s = chunk_slots(g, kv, n_tab_frames, frame_start, cslots);
+    if (s != UST_OK) return s;
+    ust::AttnArgs a{};
+    int32_t frames[UST_MAX_WINDOW_FRAMES];
+    int32_t n = 0;
+    s = plan(g, kv, frame_start, n_recent, frames, a.slots, UST_MAX_WINDOW_FRAMES, &n);
+    if (s != UST_OK) return s;
+    if (int64_t(n) * T >= (int64_t(1) << 30))
+      return fail(UST_E_SHAPE, "window too large for 32-bit key indexing");
+    const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(float(g->head_dim));
+    a.q = static_cast<const uint16_t*>(q);
+    a.cos_tab = cos_tab;
+    a.sin_tab = sin_tab;
+    a.k_cache = static_cast<const uint16_t*>(kv->k);
+    a.v_cache = static_cast<const uint16_t*>(kv->v);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse_opt;
+    a.T = T;
+    a.TV = ust_v_row_len(T);
+    a.H = g->n_heads;
+    a.D = g->head_dim;
+    a.NQ = T * g->chunk_frames;
+    a.frame_start = frame_start;
+    a.n_frames = n;
+    a.qscale = sc * 1.4426950408889634f;  // log2(e): softmax runs in base 2
+    return hip_status(ust::launch_window_attn(a, stream), "window_attn launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const void* bias,
+                            void* t_work, void* y, int32_t M, int32_t K, int32_t r, int32_t N,
+                            hipStream_t stream) {
+  try {
+    if (!x || !a || !y) return fail(UST_E_NULL, "x, a or y is NULL");
+    if (b && !t_work) return fail(UST_E_NULL, "t_work is required when b is given");
+    if (M <= 0 || K <= 0 || r <= 0 || N <= 0)
+      return fail(UST_E_SHAPE, "sizes must be positive (M=%d K=%d r=%d N=%d)", M, K, r, N);
+    if (!b && N != r) return fail(UST_E_SHAPE, "dense mode (b NULL) needs N == r");
+    if (K % 8 || r % 8 || N % 8)
+      return fail(UST_E_ALIGN, "K, r and N must be multiples of 8 (K=%d r=%d N=%d)", K, r, N);
+    if (!aligned16(x) || !aligned16(a) || !aligned16(y) || (b && !aligned16(b)) ||
+        (t_work && !aligned16(t_work)) || (bias && !aligned16(bias)))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    if (int64_t(M) * std::max(std::max(K, r), N) >= (int64_t(1) << 31) ||
+        int64_t(r) * K >= (int64_t(1) << 31) || int64_t(N) * r >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* ab = static_cast<const uint16_t*>(a);
+    const uint16_t* bb = static_cast<const uint16_t*>(b);
+    const uint16_t* biasb = static_cast<const uint16_t*>(bias);
+    if (!b) {
+      ust::GemmArgs g1{xb, ab, biasb, static_cast<uint16_t*>(y), M, r, K};
+      return hip_status(ust::launch_gemm_nt(g1, stream), "lowrank_proj launch");
+    }
+    uint16_t* t = static_cast<uint16_t*>(t_work);
+    ust::GemmArgs g1{xb, ab, nullptr, t, M, r, K};
+    hipError_t e = ust::launch_gemm_nt(g1, stream);
+    if (e != hipSuccess) return hip_status(e, "lowrank_proj launch (X A)");
+    ust::GemmArgs g2{t, bb, biasb, static_cast<uint16_t*>(y), M, N, r};
+    return hip_status(ust::launch_gemm_nt(g2, stream), "lowrank_proj launch (T B)");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI entry points (ust_host.cpp) and the
+// kernel launchers (*.hip).  Arguments reaching a launcher are validated.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ust.h"
+
+namespace ust {
+
+struct RopeTableArgs {
+  float* cos_out;
+  float* sin_out;
+  int32_t n_frames, grid_h, grid_w;
+  int32_t pairs_t, pairs_h, pairs_w;
+  double theta;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;     // [C*T][H][D]
+  const uint16_t* v_new;     // [C*T][H][D]
+  const float* cos_tab;      // [F][T][P]
+  const float* sin_tab;
+  uint16_t* k_cache;         // [slots][H][T][D]
+  uint16_t* v_cache;         // [slots][H][D][TV]
+  int32_t T, TV, H, D, C;
+  int32_t frame_start;
+  int32_t chunk_slot[8];     // slot of each chunk frame (C <= 8)
+};
+
+struct AttnArgs {
+  const uint16_t* q;         // [NQ][H][D] un-rotated
+  const float* cos_tab;      // [F][T][P]
+  const float* sin_tab;
+  const uint16_t* k_cache;   // [slots][H][T][D]
+  const uint16_t* v_cache;   // [slots][H][D][TV]
+  uint16_t* out;             // [NQ][H][D]
+  float* lse;                // [H][NQ] or nullptr
+  int32_t T, TV, H, D, NQ;
+  int32_t frame_start;       // absolute frame of query token 0
+  int32_t n_frames;          // frames in the window
+  float qscale;              // scale * log2(e), folded into the rotated query
+  int32_t slots[UST_MAX_WINDOW_FRAMES];
+};
+
+struct GemmArgs {
+  const uint16_t* x;         // [M][K]
+  const uint16_t* w;         // [N][K]
+  const uint16_t* bias;      // [N] or nullptr
+  uint16_t* y;               // [M][N]
+  int32_t M, N, K;
+};
+
+hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
+
+}  // namespace ust

@@ -1,0 +1,181 @@
+"""Device-side drivers of the windowed chunk-attention path.
+
+Thin Python over the C ABI (libust.so): allocation of the caller-owned
+buffers with torch (device memory and streams only), and the order of calls
+for one layer-chunk and for a whole clip.  Every arithmetic step runs in the
+library's kernels.
+
+Layer-chunk (UnStep, abstract): the value projection is the truncated-SVD
+product (X A_r) B_r; the chunk's keys are RoPE'd and appended with the values
+to the frame-slot ring; the chunk's queries attend over the limited window;
+the output projection is again (O A_r) B_r.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+
+# ------------------------------------------------------------------ tensors
+
+def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 device tensor (same bits)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def from_device_bf16(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def output_major(bits: np.ndarray) -> np.ndarray:
+    """[in][out] weight bits -> [out][in] (the layout the projection reads)."""
+    return np.ascontiguousarray(bits.T)
+
+
+# ------------------------------------------------------------------ state
+
+class Ring:
+    """Caller-owned KV ring: keys [n_slots][H][T][D], values [n_slots][H][D][TV]."""
+
+    def __init__(self, g: B.Geom, n_slots: int, n_sink: int, device="cuda",
+                 fill_bits: Optional[int] = None):
+        T = g.grid_h * g.grid_w
+        self.T = T
+        self.TV = B.ust_v_row_len(T)
+        self.k = torch.empty((n_slots, g.n_heads, T, g.head_dim),
+                             dtype=torch.bfloat16, device=device)
+        self.v = torch.empty((n_slots, g.n_heads, g.head_dim, self.TV),
+                             dtype=torch.bfloat16, device=device)
+        if fill_bits is not None:
+            self.fill(fill_bits)
+        self.n_slots, self.n_sink = n_slots, n_sink
+        self.abi = B.kv(self.k, self.v, n_slots, n_sink)
+
+    def fill(self, bits: int) -> None:
+        val = np.array([bits], dtype=np.uint16).view(np.int16)[0]
+        self.k.view(torch.int16).fill_(int(val))
+        self.v.view(torch.int16).fill_(int(val))
+
+    def host_k(self) -> np.ndarray:
+        return from_device_bf16(self.k)
+
+    def host_v_natural(self) -> np.ndarray:
+        """Values as [n_slots][H][T][D] bits (transposed back for comparison)."""
+        v = from_device_bf16(self.v)[..., :self.T]
+        return np.ascontiguousarray(v.transpose(0, 1, 3, 2))
+
+
+class RopeTable:
+    """Cached fp32 cos/sin [n_frames][grid_h][grid_w][P] built on the GPU."""
+
+    def __init__(self, g: B.Geom, n_frames: int, theta: float, device="cuda"):
+        P = g.head_dim // 2
+        self.n_frames = n_frames
+        self.cos = torch.empty((n_frames, g.grid_h, g.grid_w, P), dtype=torch.float32,
+                               device=device)
+        self.sin = torch.empty_like(self.cos)
+        B.ust_rope_table_build(g, n_frames, theta, self.cos, self.sin)
+
+
+@dataclass
+class LowRank:
+    """Factors of one projection on the device, output-major: a [r][K], b [N][r]
+    (b None for a dense weight given as a [N][K])."""
+    a: torch.Tensor
+    b: Optional[torch.Tensor]
+
+    @property
+    def rank(self) -> int:
+        return self.a.shape[0]
+
+    @property
+    def k_in(self) -> int:
+        return self.a.shape[1]
+
+    @property
+    def n_out(self) -> int:
+        return self.b.shape[0] if self.b is not None else self.a.shape[0]
+
+    @staticmethod
+    def from_bits(a_bits: np.ndarray, b_bits: Optional[np.ndarray], device="cuda"):
+        """a_bits [K][r] (= A_r), b_bits [r][N] (= B_r) or None."""
+        a = to_device_bf16(output_major(a_bits), device)
+        b = to_device_bf16(output_major(b_bits), device) if b_bits is not None else None
+        return LowRank(a, b)
+
+
+def lowrank_apply(p: LowRank, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                  t_work: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, p.n_out), dtype=torch.bfloat16, device=x.device)
+    if p.b is not None and t_work is None:
+        t_work = torch.empty((M, p.rank), dtype=torch.bfloat16, device=x.device)
+    B.ust_lowrank_proj(x, p.a, p.b, None, t_work, y, M, p.k_in, p.rank, p.n_out)
+    return y
+
+
+# ------------------------------------------------------------------ layer-chunk
+
+@dataclass
+class LayerBuffers:
+    """Per-call output and scratch buffers, allocated once."""
+    v: torch.Tensor        # [NQ][H*D]
+    o: torch.Tensor        # [NQ][H*D]
+    y: torch.Tensor        # [NQ][H*D]
+    t_v: Optional[torch.Tensor]
+    t_o: Optional[torch.Tensor]
+    lse: Optional[torch.Tensor]
+
+    @staticmethod
+    def alloc(n_q: int, hidden: int, n_heads: int, rank_v: Optional[int],
+              rank_o: Optional[int], with_lse: bool = False, device="cuda"):
+        bf = dict(dtype=torch.bfloat16, device=device)
+        return LayerBuffers(
+            v=torch.empty((n_q, hidden), **bf), o=torch.empty((n_q, hidden), **bf),
+            y=torch.empty((n_q, hidden), **bf),
+            t_v=torch.empty((n_q, rank_v), **bf) if rank_v else None,
+            t_o=torch.empty((n_q, rank_o), **bf) if rank_o else None,
+            lse=torch.empty((n_heads, n_q), dtype=torch.float32, device=device)
+            if with_lse else None)
+
+
+def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
+                q: torch.Tensor, k_new: torch.Tensor, wv: LowRank, wo: LowRank,
+                frame_start: int, n_recent: int, bufs: LayerBuffers,
+                scale: float = 0.0) -> torch.Tensor:
+    """One layer-chunk of the path; returns the output projection Y [NQ][H*D].
+
+    x: hidden states [NQ][hidden]; q, k_new: [NQ][H*D] un-rotated (from the
+    dense query/key projections)."""
+    lowrank_apply(wv, x, bufs.v, bufs.t_v)
+    B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,
+                    table.n_frames, frame_start)
+    B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames,
+                      frame_start, n_recent, scale, bufs.o, bufs.lse)
+    lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
+    return bufs.y
+
+
+# ------------------------------------------------------------------ clip
+
+def clip_forwards(n_chunks: int, first_steps: int, later_steps: int,
+                  clean_pass: bool) -> List[Tuple[int, int, bool]]:
+    """(chunk, forward index, is clean-cache forward) in execution order
+    (UnStep, Table 3: the first chunk runs first_steps denoising forwards, the
+    later chunks later_steps, and each chunk one clean-cache forward that
+    writes the cache last)."""
+    seq = []
+    for c in range(n_chunks):
+        n = first_steps if c == 0 else later_steps
+        seq.extend((c, i, False) for i in range(n))
+        if clean_pass:
+            seq.append((c, n, True))
+    return seq

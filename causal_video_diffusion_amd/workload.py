@@ -115,7 +115,19 @@ WAN_720P = Workload(wid=4, name="wan_720p", grid_h=45, grid_w=80, n_heads=12,
                     chunk_frames=3, n_chunks=7, n_slots=15, n_sink=3,
                     n_recent=9, rank=256, n_tab_frames=21)
 
-ALL = {w.name: w for w in (TINY, TINY_WRAP, WAN_FULL, WAN_WINDOW, WAN_CLIP, WAN_720P)}
+# Test geometries small enough for a full element-by-element oracle compare,
+# yet spanning several query tiles (312 = 2*128 + 56 queries), key tiles that
+# straddle frames (104 tokens/frame), a ragged last key tile, and a ring that
+# wraps (12 slots, 3 sinks).
+MID = Workload(wid=5, name="mid", grid_h=8, grid_w=13, n_heads=12, head_dim=128,
+               pairs=(22, 21, 21), theta=10000.0, chunk_frames=3, n_chunks=6,
+               n_slots=12, n_sink=3, n_recent=6, rank=64, n_tab_frames=18)
+MID64 = Workload(wid=6, name="mid64", grid_h=4, grid_w=10, n_heads=4, head_dim=64,
+                 pairs=(12, 10, 10), theta=10000.0, chunk_frames=3, n_chunks=5,
+                 n_slots=8, n_sink=1, n_recent=4, rank=32, n_tab_frames=15)
+
+ALL = {w.name: w for w in (TINY, TINY_WRAP, WAN_FULL, WAN_WINDOW, WAN_CLIP, WAN_720P,
+                           MID, MID64)}
 
 
 # ---------------------------------------------------------------- bf16 bits

@@ -1,0 +1,203 @@
+/*
+ * ust.h - windowed chunk attention for causal video diffusion on MI355X.
+ *
+ * The per-chunk DiT self-attention path of UnStep (arXiv 2609.32518,
+ * "UnStep: Training-Free Acceleration of Causal Video Diffusion with Fewer
+ * Steps Than Distillation"), as a C ABI over hand-written gfx950 kernels:
+ *
+ *   ust_rope_table_build  cos/sin coefficients of the 3-D RoPE, cached once
+ *                         (abstract: fused RoPE "with cached coefficients")
+ *   ust_kv_append         RoPE the chunk's keys and store keys and values in
+ *                         the frame slots of a KV ring (abstract: KV cache,
+ *                         "KV indexing")
+ *   ust_window_attn       RoPE the chunk's queries and attend over the limited
+ *                         temporal window: sink frames, recent frames, and
+ *                         the chunk itself, bidirectional inside the window
+ *                         (abstract: "limiting the temporal window retained in
+ *                         the attention KV cache"; chunks of three latent
+ *                         frames, Table 3)
+ *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
+ *                         projections (abstract; Table 5 caption)
+ *
+ * Conventions (all entry points):
+ *  - Device pointers are caller-owned.  The library never allocates, frees
+ *    or keeps them past the call.  No entry point allocates device memory.
+ *  - Every call validates all of its arguments on the host before anything
+ *    is launched; on an error nothing is launched, the status says which
+ *    class of error, and ust_last_error() (thread-local) gives the detail.
+ *  - Work is queued asynchronously on `stream` (0 = the null stream) and the
+ *    call returns without synchronising.  Buffers must stay valid until the
+ *    stream has passed the work.  A fault inside a kernel surfaces at the
+ *    caller's next synchronisation, not here.
+ *  - bf16 is bfloat16 (1-8-7) stored as 16-bit words; fp32 is IEEE binary32.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - The library holds no mutable global state and is safe to call from
+ *    several host threads (each on its own stream).
+ *  - No C++ exception crosses the ABI.
+ *
+ * Token order: a chunk has chunk_frames * T tokens, T = grid_h * grid_w.
+ * Token n is latent frame frame_start + n / T at row y = (n % T) / grid_w,
+ * column x = (n % T) % grid_w.  Per-token head vectors are stored
+ * [chunk_frames * T][n_heads][head_dim] (the row-major output of a projection
+ * to n_heads * head_dim columns).
+ */
+#ifndef UST_H
+#define UST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ust_status {
+  UST_OK = 0,
+  UST_E_NULL = 1,        /* a required pointer is NULL                         */
+  UST_E_SHAPE = 2,       /* a size is non-positive or sizes disagree           */
+  UST_E_RANGE = 3,       /* a frame lies outside the RoPE table, or a window
+                            frame is no longer held by the ring                */
+  UST_E_ALIGN = 4,       /* a device pointer is not 16-byte aligned            */
+  UST_E_UNSUPPORTED = 5, /* well-formed but not supported (see each call)      */
+  UST_E_HIP = 6          /* a HIP runtime call failed (e.g. the launch)        */
+} ust_status;
+
+/* Geometry of one DiT self-attention layer.
+ * The head dimension is split into P = head_dim / 2 rotation pairs: the first
+ * pairs_t rotate with the latent-frame index, the next pairs_h with the token
+ * row, the last pairs_w with the token column; pair j of an axis with n pairs
+ * turns by position * theta^(-j/n).  Pairs are adjacent elements (2p, 2p+1).
+ * (The axis split is the 3-D RoPE of the Wan-family DiT the paper runs,
+ * Table 1 caption.) */
+typedef struct ust_geom {
+  int32_t grid_h, grid_w;            /* tokens per latent frame T = grid_h*grid_w */
+  int32_t n_heads, head_dim;         /* head_dim must be 64 or 128                */
+  int32_t pairs_t, pairs_h, pairs_w; /* pairs_t + pairs_h + pairs_w == head_dim/2 */
+  int32_t chunk_frames;              /* latent frames per causal chunk (3)        */
+} ust_geom;
+
+/* KV ring, caller-owned device memory.  One slot per latent frame.
+ * Frame f lives in slot f if f < n_sink (sink frames are pinned), else in
+ * slot n_sink + (f - n_sink) mod (n_slots - n_sink).
+ *   k: bf16 [n_slots][n_heads][T][head_dim]        RoPE-rotated keys
+ *   v: bf16 [n_slots][n_heads][head_dim][ust_v_row_len(T)]
+ *      values stored transposed (dimension-major, token fastest); entries at
+ *      token >= T are padding that no call reads or writes. */
+typedef struct ust_kv {
+  void* k;
+  void* v;
+  int32_t n_slots;
+  int32_t n_sink;
+} ust_kv;
+
+/* Most frames one window may hold (sink + recent + chunk). */
+#define UST_MAX_WINDOW_FRAMES 128
+
+/* Tokens per row of the transposed value cache: T rounded up to a multiple
+ * of 64.  Returns -1 if T <= 0. */
+int32_t ust_v_row_len(int32_t tokens_per_frame);
+
+/* Build the cached RoPE coefficients (abstract: fused RoPE with cached
+ * coefficients).  For every frame f < n_frames, row y, column x and pair p,
+ * angle = pos * theta^(-j/n) with (pos, j, n) given by p's axis as in
+ * ust_geom; computed in fp64 and rounded to fp32.
+ *   cos_out, sin_out: fp32 [n_frames][grid_h][grid_w][head_dim/2], written.
+ * Errors: NULL pointers; n_frames <= 0 or bad geometry (UST_E_SHAPE);
+ * theta <= 0 (UST_E_RANGE); head_dim not 64/128 (UST_E_UNSUPPORTED). */
+ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double theta,
+                                float* cos_out, float* sin_out, hipStream_t stream);
+
+/* Append one chunk to the KV ring (abstract: KV cache and KV indexing).
+ * For every token n of the chunk (frame f = frame_start + n / T at (y, x))
+ * and head h:
+ *   kv.k[slot(f)][h][n % T][:]  = bf16_rne(RoPE(f, y, x) k_new[n][h][:])
+ *   kv.v[slot(f)][h][:][n % T]  = v_new[n][h][:]          (bit copy)
+ * The rotation is done in fp32 with the table's coefficients.  Slots of
+ * other frames are not touched.
+ *   k_new, v_new: bf16 [chunk_frames*T][n_heads][head_dim], read.
+ *   cos_tab, sin_tab: the table of ust_rope_table_build over n_tab_frames.
+ * Errors: NULL pointers; frame_start < 0 or the chunk's frames not all
+ * < n_tab_frames (UST_E_RANGE); n_slots - n_sink < chunk_frames or
+ * n_sink < 0 (UST_E_RANGE); misaligned pointers; T not a multiple of 8 or
+ * head_dim not 64/128 (UST_E_UNSUPPORTED). */
+ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv,
+                         const void* k_new, const void* v_new,
+                         const float* cos_tab, const float* sin_tab,
+                         int32_t n_tab_frames, int32_t frame_start,
+                         hipStream_t stream);
+
+/* Chunk-causal attention over the limited window (abstract: limited temporal
+ * window in the KV cache; Table 3: chunks of three latent frames).
+ * Window W = the prior frames f < frame_start with f < n_sink or
+ * f >= frame_start - n_recent (n_recent = -1: every prior frame), each once,
+ * then the chunk's own frames; see ust_window_plan.  The chunk's keys and
+ * values must already be appended.  For every query token n and head h:
+ *   q' = RoPE(f, y, x) q[n][h]
+ *   s_m = scale * <q', kv.k[m]> over every key m of every frame of W
+ *   out[n][h] = sum_m softmax(s)_m kv.v[m]
+ * There is no mask inside the window.  scale = 0 selects 1/sqrt(head_dim).
+ * Arithmetic: bf16 MFMA products with fp32 accumulation and fp32 softmax;
+ * the rotated, scaled query and the probabilities are rounded to bf16.
+ *   q:   bf16 [chunk_frames*T][n_heads][head_dim], un-rotated, read.
+ *   out: bf16, same layout, written.
+ *   lse_opt: NULL, or fp32 [n_heads][chunk_frames*T]: ln sum_m exp(s_m).
+ * Errors: as ust_kv_append, plus UST_E_RANGE when a window frame is no longer
+ * held by the ring (its slot was reused by a later frame up to
+ * frame_start + chunk_frames - 1) or the window exceeds
+ * UST_MAX_WINDOW_FRAMES frames; n_recent < -1 (UST_E_RANGE). */
+ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
+                           const float* cos_tab, const float* sin_tab,
+                           int32_t n_tab_frames, int32_t frame_start,
+                           int32_t n_recent, float scale, void* out,
+                           float* lse_opt, hipStream_t stream);
+
+/* Low-rank projection Y = (X A_r) B_r (+ bias) (abstract: truncated SVD of
+ * the attention value and output projections).
+ *   x:    bf16 [M][K], read.
+ *   a:    bf16 [r][K]: A_r stored output-major (row j = column j of A_r), as
+ *         a linear layer stores its weight.  Read.
+ *   b:    bf16 [N][r]: B_r stored output-major, or NULL for the dense
+ *         projection Y = X A (then N must equal r and t_work may be NULL).
+ *   bias: bf16 [N] or NULL.
+ *   t_work: bf16 [M][r] scratch, caller-owned, required when b != NULL;
+ *         receives T = X A_r rounded to bf16 (the contents are unspecified
+ *         after the call).
+ *   y:    bf16 [M][N], written.
+ * Arithmetic: bf16 MFMA with fp32 accumulation; T is rounded to bf16 between
+ * the two products.  Errors: NULL pointers; non-positive sizes (UST_E_SHAPE);
+ * K, r or N not a multiple of 8, misaligned pointers (UST_E_ALIGN); b NULL
+ * with N != r (UST_E_SHAPE). */
+ust_status ust_lowrank_proj(const void* x, const void* a, const void* b,
+                            const void* bias, void* t_work, void* y,
+                            int32_t M, int32_t K, int32_t r, int32_t N,
+                            hipStream_t stream);
+
+/* ---- host-only helpers (no GPU needed) ---- */
+
+/* Ring slot of latent frame `frame`; -1 if frame < 0 or the ring is invalid
+ * (n_sink < 0 or n_slots <= n_sink). */
+int32_t ust_slot_of_frame(const ust_kv* kv, int32_t frame);
+
+/* The window of the chunk starting at frame_start, as ust_window_attn uses
+ * it: frames_out[i] ascending, slots_out[i] = ust_slot_of_frame(frames[i]).
+ * Writes at most cap entries and the count to *n_out.
+ * Errors: NULL pointers; cap too small (UST_E_SHAPE); a window frame no
+ * longer held by the ring, n_recent < -1, frame_start < 0, or more than
+ * UST_MAX_WINDOW_FRAMES frames (UST_E_RANGE). */
+ust_status ust_window_plan(const ust_geom* g, const ust_kv* kv, int32_t frame_start,
+                           int32_t n_recent, int32_t* frames_out, int32_t* slots_out,
+                           int32_t cap, int32_t* n_out);
+
+/* Static text naming a status. */
+const char* ust_status_str(ust_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ust_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UST_H */

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle on
+the same seeded bf16 inputs.
+
+Bar: bit-exact for slot indexing, window plans, value copies and untouched
+slots; keys within one bf16 ulp; bf16 outputs within max-abs 2e-2 and
+relative-L2 1e-2 of the fp64 oracle; the fp32 RoPE table within one fp32
+ulp.  Small geometries are compared element by element; the full-size
+workloads in full for the steady-state chunk the benchmark times and on
+sampled query rows elsewhere (attention rows are independent, so a sampled
+row is exact for that row).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_video_diffusion_amd as cvd
+from causal_video_diffusion_amd import _binding as B
+from causal_video_diffusion_amd import path as P
+from causal_video_diffusion_amd import workload as wl
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+NAN_BITS = 0x7FC1          # a quiet-NaN sentinel for untouched memory
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load()
+
+
+def _g(w):
+    return cvd.geom(*w.geom_tuple())
+
+
+def _f64(bits):
+    return wl.bf16_bits_to_f64(bits)
+
+
+def assert_close(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, what
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = got - ref
+    ma = float(np.max(np.abs(d)))
+    rl = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    print(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert ma <= max_abs and rl <= rel_l2, f"{what}: max_abs {ma:.3e}, rel_l2 {rl:.3e}"
+
+
+def _bf16_ulp(x):
+    _, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(1.0, e - 8)
+
+
+def _sample_rows(n, k=192, seed=0):
+    """First, last (ragged tail) and random rows."""
+    if n <= k:
+        return np.arange(n)
+    rs = np.random.default_rng(seed)
+    mid = rs.choice(np.arange(64, n - 64), size=k - 128, replace=False)
+    return np.unique(np.concatenate([np.arange(64), mid, np.arange(n - 64, n)]))
+
+
+# ------------------------------------------------------------------ RoPE table
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "wan_window", "wan_720p"])
+def test_rope_table(name):
+    w = wl.ALL[name]
+    print(f"[rope_table {name}]", flush=True)
+    t = P.RopeTable(_g(w), w.n_tab_frames, w.theta)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    for got, ref in ((t.cos, c_ref), (t.sin, s_ref)):
+        g = got.cpu().numpy().astype(np.float64)
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(g - ref) <= ulp + 1e-300)
+
+
+# ------------------------------------------------------------------ KV append
+
+def _append_all(w, n_chunks=None, tokens=None):
+    """Append every chunk on the GPU and in the oracle; yields per chunk."""
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    for c in range(n_chunks or w.n_chunks):
+        kb = wl.chunk_tokens(w, wl.TAG_K, c)
+        vb = wl.chunk_tokens(w, wl.TAG_V, c)
+        B.ust_kv_append(g, ring.abi, P.to_device_bf16(kb), P.to_device_bf16(vb),
+                        table.cos, table.sin, w.n_tab_frames, 3 * c)
+        O.kv_append(cache, _f64(kb), _f64(vb), cos, sin, 3 * c, 3, w.grid_h,
+                    w.grid_w, w.n_slots, w.n_sink)
+        yield c, g, table, ring, cache, (cos, sin), kb, vb
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wrap", "mid", "mid64", "wan_720p"])
+def test_kv_append(name):
+    w = wl.ALL[name]
+    print(f"[kv_append {name}]", flush=True)
+    written = {}
+    kin = {}
+    for c, g, table, ring, cache, _, kb, vb in _append_all(w):
+        for i in range(3):
+            written[O.slot_of_frame(3 * c + i, w.n_slots, w.n_sink)] = 3 * c + i
+            kin[3 * c + i] = _f64(kb[i * w.T:(i + 1) * w.T]).transpose(1, 0, 2)
+        torch.cuda.synchronize()
+        gk = ring.host_k()
+        gv_raw = P.from_device_bf16(ring.v)
+        gv = ring.host_v_natural()
+        for s in range(w.n_slots):
+            if s not in written:        # untouched slots keep the sentinel, bit for bit
+                assert np.all(gk[s] == NAN_BITS) and np.all(gv_raw[s] == NAN_BITS)
+                continue
+            # The rotation runs in fp32 from fp32 coefficients, then rounds to
+            # bf16: the error is one bf16 ulp of the result plus the fp32
+            # rounding of the rotation, ~2^-23 (|a| + |b|) for the pair (a, b)
+            # (visible when a rotated pair nearly cancels).
+            ref_k = cache.k[s]
+            got_k = _f64(gk[s])
+            src = kin[written[s]]
+            pair = np.abs(src[..., 0::2]) + np.abs(src[..., 1::2])
+            fp32_err = np.repeat(pair, 2, axis=-1) * 2.0 ** -21
+            assert np.all(np.abs(got_k - ref_k) <= _bf16_ulp(ref_k) + fp32_err), f"slot {s} keys"
+            assert_close(got_k, ref_k, f"slot {s} keys")
+            # values are a bit copy of the appended bf16 values
+            f = written[s]
+            cc, i = divmod(f, 3)
+            src = wl.chunk_tokens(w, wl.TAG_V, cc)[i * w.T:(i + 1) * w.T]
+            assert np.array_equal(gv[s], src.transpose(1, 0, 2)), f"slot {s} values"
+        # the padding past T in every transposed value row is never written
+        assert np.all(gv_raw[..., w.T:] == NAN_BITS)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True):
+    q = P.to_device_bf16(qb)
+    out = torch.empty_like(q)
+    l = torch.empty((w.n_heads, w.n_q), dtype=torch.float32, device="cuda") if lse else None
+    B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
+                      w.n_recent if n_recent is None else n_recent, 0.0, out, l)
+    torch.cuda.synchronize()
+    return P.from_device_bf16(out), (l.cpu().numpy() if lse else None)
+
+
+def _attn_case(name, full_chunks=(), rows_per_chunk=192):
+    w = wl.ALL[name]
+    for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        rows = np.arange(w.n_q) if (c in full_chunks or w.n_q <= 512) else \
+            _sample_rows(w.n_q, rows_per_chunk, seed=c)
+        print(f"[attn {name} chunk {c}: {len(rows)} rows]", flush=True)
+        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c)
+        o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
+                                       w.grid_w, w.n_slots, w.n_sink, w.n_recent,
+                                       rows=rows)
+        assert_close(_f64(o_gpu[rows]), o_ref, f"{name} chunk {c} O")
+        assert_close(lse_gpu[:, rows], lse_ref, f"{name} chunk {c} lse", max_abs=2e-2,
+                     rel_l2=1e-3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wrap", "mid", "mid64"])
+def test_window_attn_full_compare(name):
+    _attn_case(name)
+
+
+def test_window_attn_wan_window():
+    # chunk 5 is the steady-state chunk the benchmark times: compared in full
+    _attn_case("wan_window", full_chunks=(5,))
+
+
+def test_window_attn_wan_full_cache():
+    _attn_case("wan_full")
+
+
+def test_window_attn_wan_720p():
+    _attn_case("wan_720p")
+
+
+def test_window_edge_cases():
+    """n_recent = 0 (sinks + chunk), n_recent past the start (= full causal),
+    no sinks, and the chunk-0 window (only the chunk itself)."""
+    base = wl.MID
+    for w in (base.replace(n_recent=0), base.replace(n_recent=30, n_slots=18),
+              base.replace(n_sink=0, n_slots=9), base.replace(n_recent=-1, n_slots=18)):
+        print(f"[edge n_sink={w.n_sink} n_recent={w.n_recent} n_slots={w.n_slots}]", flush=True)
+        for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
+            qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+            o_gpu, _ = _attn_gpu(g, w, ring, table, qb, c, lse=False)
+            o_ref, _ = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
+                                     w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+            assert_close(_f64(o_gpu), o_ref, f"edge chunk {c}")
+
+
+def test_nan_outside_window_and_determinism():
+    """Poisoning every slot outside the window (and the value padding) with NaN
+    leaves the output bit-identical; two runs agree bit for bit."""
+    w = wl.MID
+    for c, g, table, ring, cache, _, kb, vb in _append_all(w):
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        o1, l1 = _attn_gpu(g, w, ring, table, qb, c)
+        o2, l2 = _attn_gpu(g, w, ring, table, qb, c)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        _, slots = O.window_slots(3 * c, 3, w.n_sink, w.n_recent, w.n_slots)
+        keep_k = ring.k[slots].clone()
+        keep_v = ring.v[slots].clone()
+        ring.fill(NAN_BITS)
+        ring.k[slots] = keep_k
+        ring.v[slots] = keep_v
+        ring.v[..., w.T:].view(torch.int16).fill_(NAN_BITS)
+        o3, l3 = _attn_gpu(g, w, ring, table, qb, c)
+        assert np.array_equal(o1, o3) and np.array_equal(l1, l3), f"chunk {c}"
+        if c == 3:
+            break
+
+
+def test_v_one_gives_one_and_k_zero_gives_mean():
+    w = wl.MID
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    ones = np.full((w.n_q, w.n_heads, w.head_dim), 0x3F80, np.uint16)
+    zeros = np.zeros((w.n_q, w.n_heads, w.head_dim), np.uint16)
+    for c in range(4):
+        kb = wl.chunk_tokens(w, wl.TAG_K, c)
+        B.ust_kv_append(g, ring.abi, P.to_device_bf16(kb), P.to_device_bf16(ones),
+                        table.cos, table.sin, w.n_tab_frames, 3 * c)
+    qb = wl.chunk_tokens(w, wl.TAG_Q, 3)
+    q4 = wl.f32_to_bf16_bits((_f64(qb) * 4).astype(np.float32))   # peaky scores
+    o, _ = _attn_gpu(g, w, ring, table, q4, 3)
+    assert np.max(np.abs(_f64(o) - 1.0)) <= 2 ** -7
+    # K = 0: uniform weights, O = mean of the window's values, lse = ln(keys)
+    ring2 = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    vs = []
+    for c in range(4):
+        vb = wl.chunk_tokens(w, wl.TAG_V, c)
+        vs.append(_f64(vb))
+        B.ust_kv_append(g, ring2.abi, P.to_device_bf16(zeros), P.to_device_bf16(vb),
+                        table.cos, table.sin, w.n_tab_frames, 3 * c)
+    o, lse = _attn_gpu(g, w, ring2, table, qb, 3)
+    frames, _ = O.window_slots(9, 3, w.n_sink, w.n_recent, w.n_slots)
+    allv = np.concatenate(vs)                      # frames 0..11, [n][H][D]
+    sel = np.concatenate([allv[f * w.T:(f + 1) * w.T] for f in frames])
+    mean = sel.mean(axis=0)                        # [H][D]
+    assert_close(_f64(o), np.broadcast_to(mean, o.shape), "K=0 mean", max_abs=1e-2)
+    assert np.max(np.abs(lse - math.log(len(frames) * w.T))) < 1e-4
+
+
+# ------------------------------------------------------------------ low rank
+
+@pytest.mark.parametrize("name,M", [("tiny", 72), ("mid", 312), ("mid", 100),
+                                    ("wan_window", 4680), ("wan_720p", 10800)])
+def test_lowrank_proj(name, M):
+    w = wl.ALL[name]
+    print(f"[lowrank {name} M={M}]", flush=True)
+    a, b = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
+    xb = wl.activations(w, 0)[:M]
+    p = P.LowRank.from_bits(a, b)
+    y = P.lowrank_apply(p, P.to_device_bf16(xb))
+    torch.cuda.synchronize()
+    ref = O.lowrank_proj(_f64(xb), _f64(a), _f64(b))
+    assert_close(_f64(P.from_device_bf16(y)), ref, f"{name} lowrank M={M}")
+
+
+def test_lowrank_dense_and_bias():
+    w = wl.WAN_FULL
+    wb = wl.dense_weight_bf16(w, wl.TAG_WV)
+    xb = wl.activations(w, 0)[:1000]
+    bias = wl.normal_bf16(w, (w.hidden,), 99)
+    x = P.to_device_bf16(xb)
+    a = P.to_device_bf16(P.output_major(wb))
+    y = torch.empty((1000, w.hidden), dtype=torch.bfloat16, device="cuda")
+    bd = P.to_device_bf16(bias)
+    B.ust_lowrank_proj(x, a, None, bd, None, y, 1000, w.hidden, w.hidden, w.hidden)
+    torch.cuda.synchronize()
+    ref = O.lowrank_proj(_f64(xb), _f64(wb), None, _f64(bias))
+    assert_close(_f64(P.from_device_bf16(y)), ref, "dense + bias")
+
+
+# ------------------------------------------------------------------ layer-chunk
+
+def test_layer_chunk_wan_window_chained():
+    """V projection -> append -> attention -> O projection, chained on the
+    GPU, against the same chain in fp64 (no intermediate rounding)."""
+    w = wl.WAN_WINDOW
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
+    ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, w.rank)
+    wv, wo = P.LowRank.from_bits(av, bv), P.LowRank.from_bits(ao, bo)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank)
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    for c in range(w.n_chunks):
+        xb = wl.activations(w, c)
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        kb = wl.chunk_tokens(w, wl.TAG_K, c)
+        y = P.layer_chunk(g, ring, table, P.to_device_bf16(xb),
+                          P.to_device_bf16(qb.reshape(w.n_q, -1)),
+                          P.to_device_bf16(kb.reshape(w.n_q, -1)), wv, wo, 3 * c,
+                          w.n_recent, bufs)
+        torch.cuda.synchronize()
+        v_ref = O.lowrank_proj(_f64(xb), _f64(av), _f64(bv)).reshape(w.n_q, w.n_heads, -1)
+        O.kv_append(cache, _f64(kb), v_ref, cos, sin, 3 * c, 3, w.grid_h, w.grid_w,
+                    w.n_slots, w.n_sink)
+        if c < 3:
+            continue
+        rows = _sample_rows(w.n_q, 160, seed=10 + c)
+        o_ref, _ = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h, w.grid_w,
+                                 w.n_slots, w.n_sink, w.n_recent, rows=rows)
+        y_ref = O.lowrank_proj(o_ref.reshape(len(rows), -1), _f64(ao), _f64(bo))
+        print(f"[layer_chunk wan_window chunk {c}]", flush=True)
+        assert_close(_f64(P.from_device_bf16(y))[rows], y_ref, f"chunk {c} Y")

@@ -1,0 +1,178 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host-side integer work (slot map, window plan, argument
+validation) matches the oracle bit for bit.  No kernel is launched here:
+every call below is rejected or answered on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_video_diffusion_amd as cvd
+from causal_video_diffusion_amd import _binding as B
+from causal_video_diffusion_amd import workload as wl
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from causal_video_diffusion_amd import build
+        build.build()
+    return B.load()
+
+
+def _header_symbols():
+    txt = open(os.path.join(ROOT, "include", "ust.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ust_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = _header_symbols()
+    assert len(syms) == 9
+    assert sorted(B.EXPORTS) == syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def _geom(w):
+    return cvd.geom(*w.geom_tuple())
+
+
+def test_slot_of_frame_bit_exact(lib):
+    for n_slots, n_sink in [(9, 1), (7, 1), (21, 3), (15, 3), (21, 0), (5, 4), (40, 7)]:
+        ring = B.Kv(None, None, n_slots, n_sink)
+        got = [B.ust_slot_of_frame(ring, f) for f in range(1000)]
+        assert got == [O.slot_of_frame(f, n_slots, n_sink) for f in range(1000)]
+    assert B.ust_slot_of_frame(B.Kv(None, None, 3, 3), 0) == -1
+    assert B.ust_slot_of_frame(B.Kv(None, None, 8, 1), -1) == -1
+
+
+def test_window_plan_bit_exact_exhaustive(lib):
+    g = _geom(wl.TINY)
+    n = 0
+    for n_slots in range(4, 16):
+        for n_sink in range(0, 4):
+            if n_sink >= n_slots:
+                continue
+            ring = B.Kv(None, None, n_slots, n_sink)
+            for n_recent in (-1, 0, 1, 2, 3, 6, 9):
+                for f0 in range(0, 45):
+                    try:
+                        want = O.window_slots(f0, 3, n_sink, n_recent, n_slots)
+                    except ValueError:
+                        want = None
+                    if want is not None and len(want[0]) > B.UST_MAX_WINDOW_FRAMES:
+                        want = None
+                    if want is None:
+                        with pytest.raises(cvd.UstError) as e:
+                            B.ust_window_plan(g, ring, f0, n_recent)
+                        assert e.value.name == "UST_E_RANGE"
+                    else:
+                        assert B.ust_window_plan(g, ring, f0, n_recent) == \
+                            (list(want[0]), list(want[1]))
+                    n += 1
+    assert n > 5000
+
+
+def test_window_plan_long_horizon(lib):
+    """Streaming far past one clip with a 15-slot ring, 3 sinks, 9 recent."""
+    g = _geom(wl.WAN_720P)
+    ring = B.Kv(None, None, 15, 3)
+    for f0 in range(0, 1000, 3):
+        assert B.ust_window_plan(g, ring, f0, 9) == \
+            tuple(list(v) for v in O.window_slots(f0, 3, 3, 9, 15))
+
+
+def test_window_plan_workloads(lib):
+    for w in (wl.TINY, wl.TINY_WRAP, wl.WAN_FULL, wl.WAN_WINDOW, wl.WAN_720P):
+        g = _geom(w)
+        ring = B.Kv(None, None, w.n_slots, w.n_sink)
+        for c in range(w.n_chunks):
+            assert B.ust_window_plan(g, ring, 3 * c, w.n_recent) == \
+                tuple(list(v) for v in O.window_slots(3 * c, 3, w.n_sink, w.n_recent,
+                                                      w.n_slots))
+
+
+def test_window_plan_errors(lib):
+    g = _geom(wl.WAN_WINDOW)
+    ring = B.Kv(None, None, 21, 3)
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, ring, -3, 6)
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, ring, 3, -2)
+    with pytest.raises(cvd.UstError, match="UST_E_SHAPE"):
+        B.ust_window_plan(g, ring, 15, 6, cap=4)
+    # a ring too small for the window
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, B.Kv(None, None, 10, 3), 15, 6)
+    # a window longer than the maximum
+    big = B.Kv(None, None, 400, 0)
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, big, 200, -1)
+
+
+def _raw(lib, name, *args):
+    st = getattr(lib, name)(*args)
+    return B.STATUS[st], lib.ust_last_error().decode()
+
+
+def test_compute_entry_points_reject_bad_arguments(lib):
+    """Validation happens before any launch, so these return without a GPU."""
+    w = wl.WAN_WINDOW
+    g = _geom(w)
+    fake = 0x10000          # aligned, never dereferenced: every call below fails validation
+    ring = B.Kv(fake, fake, 21, 3)
+    gp, rp = ctypes.byref(g), ctypes.byref(ring)
+    # NULL pointers
+    assert _raw(lib, "ust_kv_append", gp, rp, None, fake, fake, fake, 21, 0, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 0, 6, 0.0, None, None,
+                None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_rope_table_build", gp, 21, 1e4, None, fake, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_lowrank_proj", fake, fake, fake, None, None, fake, 8, 8, 8, 8,
+                None)[0] == "UST_E_NULL"
+    # frames outside the table
+    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 21, 19, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake, None,
+                None)[0] == "UST_E_RANGE"
+    # misaligned
+    assert _raw(lib, "ust_kv_append", gp, rp, fake + 2, fake, fake, fake, 21, 0, None)[0] == "UST_E_ALIGN"
+    assert _raw(lib, "ust_lowrank_proj", fake, fake, None, None, None, fake, 8, 12, 8, 8,
+                None)[0] == "UST_E_ALIGN"
+    # shapes
+    assert _raw(lib, "ust_lowrank_proj", fake, fake, None, None, None, fake, 8, 16, 8, 16,
+                None)[0] == "UST_E_SHAPE"
+    assert _raw(lib, "ust_lowrank_proj", fake, fake, None, None, None, fake, 0, 16, 8, 8,
+                None)[0] == "UST_E_SHAPE"
+    assert _raw(lib, "ust_rope_table_build", gp, 0, 1e4, fake, fake, None)[0] == "UST_E_SHAPE"
+    assert _raw(lib, "ust_rope_table_build", gp, 4, -1.0, fake, fake, None)[0] == "UST_E_RANGE"
+    # unsupported head size and token count
+    g2 = cvd.geom(30, 52, 12, 96, 16, 16, 16, 3)
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g2), rp, fake, fake, fake, fake, 21, 0,
+                None)[0] == "UST_E_UNSUPPORTED"
+    g3 = cvd.geom(3, 5, 12, 128, 22, 21, 21, 3)
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g3), rp, fake, fake, fake, fake, 21, 0,
+                None)[0] == "UST_E_UNSUPPORTED"
+    # pair split that does not add up
+    g4 = cvd.geom(30, 52, 12, 128, 22, 21, 20, 3)
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g4), rp, fake, fake, fake, fake, 21, 0,
+                None)[0] == "UST_E_SHAPE"
+    # ring that cannot hold a chunk
+    small = B.Kv(fake, fake, 4, 3)
+    assert _raw(lib, "ust_kv_append", gp, ctypes.byref(small), fake, fake, fake, fake, 21, 6,
+                None)[0] == "UST_E_RANGE"
+    # a window frame already overwritten
+    ring10 = B.Kv(fake, fake, 10, 3)
+    st, msg = _raw(lib, "ust_window_attn", gp, ctypes.byref(ring10), fake, fake, fake, 21, 15,
+                   6, 0.0, fake, None, None)
+    assert st == "UST_E_RANGE" and "no longer in the ring" in msg
+
+
+def test_status_strings(lib):
+    for k, v in B.STATUS.items():
+        assert lib.ust_status_str(k).decode() == v
+    assert lib.ust_v_row_len(1560) == 1600 and lib.ust_v_row_len(64) == 64
+    assert lib.ust_v_row_len(3600) == 3648 and lib.ust_v_row_len(0) == -1
