@@ -13,6 +13,8 @@
 
 #include "ust_internal.h"
 
+extern "C" int32_t ust_v_row_len(int32_t T);
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -68,6 +70,15 @@ ust_status check_kv(const ust_kv* kv) {
   if (kv->n_sink < 0 || kv->n_slots <= kv->n_sink)
     return fail(UST_E_RANGE, "ring needs 0 <= n_sink < n_slots (got %d, %d)", kv->n_sink,
                 kv->n_slots);
+  return UST_OK;
+}
+
+// Element offsets into the ring are 32-bit in the kernels.
+ust_status check_ring_size(const ust_geom* g, const ust_kv* kv) {
+  const int64_t T = int64_t(g->grid_h) * g->grid_w;
+  const int64_t per_slot = int64_t(g->n_heads) * g->head_dim * ust_v_row_len(int32_t(T));
+  if (int64_t(kv->n_slots) * per_slot >= (int64_t(1) << 31))
+    return fail(UST_E_SHAPE, "ring of %d slots too large for 32-bit indexing", kv->n_slots);
   return UST_OK;
 }
 
@@ -199,6 +210,8 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
     if (s != UST_OK) return s;
     s = check_kv(kv);
     if (s != UST_OK) return s;
+    s = check_ring_size(g, kv);
+    if (s != UST_OK) return s;
     if (!k_new || !v_new || !cos_tab || !sin_tab)
       return fail(UST_E_NULL, "k_new, v_new or table pointer is NULL");
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_tab) || !aligned16(sin_tab))
@@ -235,6 +248,8 @@ ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
     s = check_kv(kv);
+    if (s != UST_OK) return s;
+    s = check_ring_size(g, kv);
     if (s != UST_OK) return s;
     if (!q || !cos_tab || !sin_tab || !out)
       return fail(UST_E_NULL, "q, table or out pointer is NULL");

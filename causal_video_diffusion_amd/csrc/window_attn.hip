@@ -5,25 +5,37 @@
 //
 // Design (gfx950, wave64, bf16 MFMA 32x32x16 with fp32 accumulation):
 //  * A workgroup of 4 waves owns 128 queries of one head; each wave owns 32.
-//    The window's keys form one virtual sequence (frame after frame, each
+//    Two workgroups share a CU (2 waves per SIMD), so one wave's softmax
+//    VALU work overlaps the other's MFMA work.
+//  * The window's keys form one virtual sequence (frame after frame, each
 //    frame's T keys read from its ring slot), walked in tiles of 64 keys;
-//    only the last tile can be partial, so a tile may straddle frames.
+//    only the last tile can be partial, and a tile may straddle frames.
 //  * Scores are computed transposed, S^T = K Q^T: the MFMA output puts one
 //    query per lane (column) and 16 keys per lane in registers, so the row
-//    max and row sum of the online softmax are in-lane reductions plus one
-//    swap between lane l and l^32.  The query rotation, the softmax scale and
-//    log2(e) are folded into the bf16 query fragments once per workgroup.
-//  * The A operand rows of S^T are permuted (bits 2 and 3 of the key index
+//    max and row sum are in-lane reductions plus one exchange between lanes
+//    l and l^32.  The query rotation, the softmax scale and log2(e) are
+//    folded into the bf16 query fragments once per workgroup.
+//  * The score accumulators start at -m (the lane's running reference max),
+//    so the MFMA yields s - m directly.  The reference only moves when a
+//    tile's scores exceed it by more than 2^8 (and on the first tile), so the
+//    O/l rescale is skipped on almost every tile; the final normalisation by
+//    the running sum makes the result exact regardless of the reference.
+//  * The A-operand rows of S^T are permuted (bits 2 and 3 of the key index
 //    swapped) so that each lane's 8 score registers of one 16-key group hold
-//    8 consecutive keys.  Those registers, rounded to bf16, are directly the
-//    B operand of O^T = V^T P^T; V^T comes from the transposed value cache,
-//    so neither P nor V is transposed in LDS.
-//  * K and V^T tiles are staged through LDS (XOR-swizzled 16-byte chunks,
-//    bank-conflict-free for the MFMA operand reads), double-buffered with the
-//    next tile's global loads in flight during the current tile's math.
+//    8 consecutive keys: those registers, rounded to bf16, are directly the
+//    B operand of O^T = V^T P^T.  V^T comes from the transposed value cache,
+//    so neither P nor V is transposed on chip.  The row sum is accumulated
+//    from the same bf16 pairs with v_dot2_f32_bf16.
+//  * K and V^T tiles go straight from global memory to LDS
+//    (global_load_lds_dwordx4, no register staging), double-buffered, with
+//    16-byte chunks XOR-swizzled so that every 16-lane group of an MFMA
+//    operand read touches 64 distinct banks.  Tiles inside one frame use a
+//    uniform base address plus per-lane constant offsets.
 //  * Workgroups are numbered so that each XCD (8 per chip, dispatched round
 //    robin) gets a contiguous run of (head, query tile) work: the workgroups
-//    sharing a head's K/V stream share one L2.
+//    streaming one head's K/V share an L2.
+
+#include <type_traits>
 
 #include "ust_device.h"
 #include "ust_internal.h"
@@ -34,13 +46,24 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
+constexpr float kRescale = 8.0f;  // move the reference max when exceeded (log2 units)
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // swap bits 2 and 3 of a row index within a 32-row MFMA block
 __device__ __forceinline__ int perm_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
-// XOR key of a K-tile row's 16-byte chunks (bits 0, 1, 3 of the row)
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+// XOR key of a K-tile row's 16-byte chunks: distinct across any 16 rows that
+// one 16-lane group reads (rows of 256 B for D=128, of 128 B for D=64)
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+// XOR key of a V^T-tile row (128 B: 64 keys)
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
 // Combine a value with the one held by lane l^32.  v_permlane32_swap with the
 // same register as both operands leaves, in its two results, this lane's value
@@ -62,19 +85,23 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
 }
 
+__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (lds_void*)(l), 16, 0, 0);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 window_attn_kernel(AttnArgs a) {
-  constexpr int KS = D / 16;            // k-steps of the score product
-  constexpr int DB = D / 32;            // 32-row blocks of O^T
-  constexpr int KCH = D / 8;            // 16-byte chunks per key row
-  constexpr int KITEMS = kBN * KCH / 256;   // K-tile chunks per thread
-  constexpr int VITEMS = D * 8 / 256;       // V^T-tile chunks per thread
-  constexpr int KTILE = kBN * D;        // elements per tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][KTILE];
-  __shared__ int64_t kbase[UST_MAX_WINDOW_FRAMES];
-  __shared__ int64_t vbase[UST_MAX_WINDOW_FRAMES];
+  constexpr int KS = D / 16;                          // k-steps of the score product
+  constexpr int DB = D / 32;                          // 32-row blocks of O^T
+  constexpr int KCPR = D / 8;                         // 16-byte chunks per key row
+  constexpr int KRPI = 64 / KCPR;                     // key rows per 1 KB load
+  constexpr int KINST = kBN * D * 2 / 1024 / kWaves;  // K loads per wave per tile
+  constexpr int VINST = D * kBN * 2 / 1024 / kWaves;  // V^T loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][D * kBN];
+  __shared__ uint32_t kbase[UST_MAX_WINDOW_FRAMES];
+  __shared__ uint32_t vbase[UST_MAX_WINDOW_FRAMES];
 
   const int nqt = (a.NQ + kBM - 1) / kBM;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -82,16 +109,17 @@ window_attn_kernel(AttnArgs a) {
   const int q0 = (w % nqt) * kBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int T = a.T;
+  const int TV = a.TV;
   const int nk = a.n_frames * T;
   const int ntiles = (nk + kBN - 1) / kBN;
 
   for (int i = tid; i < a.n_frames; i += 256) {
-    kbase[i] = (int64_t(a.slots[i]) * a.H + h) * T * D;
-    vbase[i] = (int64_t(a.slots[i]) * a.H + h) * D * a.TV;
+    kbase[i] = uint32_t((a.slots[i] * a.H + h) * T * D);
+    vbase[i] = uint32_t((a.slots[i] * a.H + h) * D * TV);
   }
 
   // ---- query fragments: RoPE at the query's own position, scale, bf16 ----
@@ -126,56 +154,58 @@ window_attn_kernel(AttnArgs a) {
   }
   __syncthreads();  // kbase / vbase visible
 
-  // ---- per-thread cursors of the tile chunks this thread loads ----
-  // K items: key kl = tid / KCH + (256 / KCH) * it, chunk dc = tid % KCH
-  // V items: dim d = tid / 8 + 32 * it, key chunk kc = tid % 8 (keys 8kc..8kc+7)
-  const int k_dc = tid % KCH;
-  const int k_kl0 = tid / KCH;
-  const int v_kc = tid % 8;
-  const int v_d0 = tid / 8;
-  int kf[KITEMS], kt[KITEMS];          // (window frame, token) of each K item
+  // ---- per-lane constants of the tile loads ----
+  // K load i of this wave fills LDS bytes [(wave*KINST + i) KB, +1 KB): key row
+  // krow[i], 16-byte chunk kdc[i] (logical; stored at the lane's position).
+  int krow[KINST], koff[KINST];
 #pragma unroll
-  for (int it = 0; it < KITEMS; ++it) {
-    const int m = k_kl0 + (256 / KCH) * it;
-    kf[it] = m / T;
-    kt[it] = m % T;
+  for (int i = 0; i < KINST; ++i) {
+    const int row = KRPI * (wave * KINST + i) + lane / KCPR;
+    const int dc = (lane % KCPR) ^ kswz<D>(row);
+    krow[i] = row;
+    koff[i] = row * D + dc * 8;
   }
-  int vf = (8 * v_kc) / T, vt = (8 * v_kc) % T;
+  // V^T load i: dimension vd[i], 8-key chunk vkc[i]
+  int vd[VINST], vkc[VINST], voff[VINST];
+#pragma unroll
+  for (int i = 0; i < VINST; ++i) {
+    const int d = 8 * (wave * VINST + i) + lane / 8;
+    const int kc = (lane % 8) ^ vswz(d);
+    vd[i] = d;
+    vkc[i] = kc;
+    voff[i] = d * TV + kc * 8;
+  }
 
-  uint4 kreg[KITEMS], vreg[VITEMS];
-  auto gload = [&]() {
+  // Issue the global->LDS loads of tile (fi, t0) into buffer buf.
+  auto issue = [&](int j, int fi, int t0, int buf) {
+    uint16_t* lk = &lds_k[buf][wave * KINST * 512];
+    uint16_t* lv = &lds_v[buf][wave * VINST * 512];
+    if (t0 + kBN <= T && j * kBN + kBN <= nk) {
+      // whole tile inside frame fi: uniform base + lane constants
+      const uint16_t* kb = a.k_cache + kbase[fi] + uint32_t(t0 * D);
+      const uint16_t* vb = a.v_cache + vbase[fi] + uint32_t(t0);
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      kreg[it] = make_uint4(0, 0, 0, 0);
-      if (kf[it] < a.n_frames)
-        kreg[it] = *reinterpret_cast<const uint4*>(a.k_cache + kbase[kf[it]] + int64_t(kt[it]) * D + k_dc * 8);
-    }
+      for (int i = 0; i < KINST; ++i) load_lds16(kb + koff[i], lk + i * 512);
 #pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      vreg[it] = make_uint4(0, 0, 0, 0);
-      if (vf < a.n_frames)
-        vreg[it] = *reinterpret_cast<const uint4*>(a.v_cache + vbase[vf] + int64_t(v_d0 + 32 * it) * a.TV + vt);
-    }
-  };
-  auto advance = [&]() {
+      for (int i = 0; i < VINST; ++i) load_lds16(vb + voff[i], lv + i * 512);
+    } else {
+      // straddles frames or runs past the window: per-lane frame lookup;
+      // keys past the window are pointed at the window's first key (finite
+      // data whose probability is masked to zero)
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      kt[it] += kBN;
-      while (kt[it] >= T) { kt[it] -= T; ++kf[it]; }
-    }
-    vt += kBN;
-    while (vt >= T) { vt -= T; ++vf; }
-  };
-  auto lstore = [&](int buf) {
+      for (int i = 0; i < KINST; ++i) {
+        int tt = t0 + krow[i], f = fi;
+        while (tt >= T) { tt -= T; ++f; }
+        if (f >= a.n_frames) { f = 0; tt = 0; }
+        load_lds16(a.k_cache + kbase[f] + uint32_t(tt * D) + (koff[i] - krow[i] * D), lk + i * 512);
+      }
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int kl = k_kl0 + (256 / KCH) * it;
-      *reinterpret_cast<uint4*>(&lds_k[buf][kl * D + ((k_dc ^ kswz(kl)) * 8)]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int d = v_d0 + 32 * it;
-      *reinterpret_cast<uint4*>(&lds_v[buf][d * kBN + ((v_kc ^ (d & 7)) * 8)]) = vreg[it];
+      for (int i = 0; i < VINST; ++i) {
+        int tt = t0 + 8 * vkc[i], f = fi;
+        while (tt >= T) { tt -= T; ++f; }
+        if (f >= a.n_frames) { f = 0; tt = 0; }
+        load_lds16(a.v_cache + vbase[f] + uint32_t(tt) + uint32_t(vd[i] * TV), lv + i * 512);
+      }
     }
   };
 
@@ -184,41 +214,59 @@ window_attn_kernel(AttnArgs a) {
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-  float mrow = -INFINITY;   // running max (log2 units) of this lane's query
-  float lrow = 0.f;         // this lane's share of the running sum
+  float mref = 0.f;   // reference max (log2 units) of this lane's query
+  float lrow = 0.f;   // this lane's share of the running sum, relative to mref
 
-  gload();
-  advance();
-  lstore(0);
+  int fi = 0, t0 = 0;           // frame index and token of the next tile to load
+  issue(0, fi, t0, 0);
+  t0 += kBN;
+  while (t0 >= T) { t0 -= T; ++fi; }
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    __syncthreads();
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      gload();
-      advance();
+  // Element offsets of this lane's MFMA operand fragments within a tile
+  // buffer (fixed across tiles).  Key block kb adds 32 rows (kswz is the same
+  // for rows r and r + 32) and O^T block b adds 32 dims (vswz likewise), so
+  // those and the buffer index fold into the ds_read immediate offsets.
+  int koffr[KS], voffr[4];
+  {
+    const int row = perm_row(l32);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) koffr[s] = row * D + (((2 * s + half) ^ kswz<D>(row)) * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) voffr[q] = l32 * kBN + (((2 * q + half) ^ vswz(l32)) * 8);
+  }
+
+  // One tile: scores, online softmax, PV.  MASKED is the last tile, whose
+  // keys past the window end get probability zero.
+  auto tile = [&](int j, auto masked_tag, auto buf_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int buf = decltype(buf_tag)::value;   // == j & 1
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile j are in LDS
+    __syncthreads();                 // ... and every wave's; buf^1 is free
+    if (!MASKED && j + 1 < ntiles) {
+      issue(j + 1, fi, t0, buf ^ 1);
+      t0 += kBN;
+      while (t0 >= T) { t0 -= T; ++fi; }
     }
+    const uint16_t* K = lds_k[buf];
+    const uint16_t* V = lds_v[buf];
 
-    // ---- S^T = K Q^T for the tile's two 32-key blocks ----
+    // ---- S^T - mref = K Q^T + (-mref), two 32-key blocks ----
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const int kl = 32 * kb + perm_row(l32);
-      const uint16_t* krow = &lds_k[buf][kl * D];
-      const int sw = kswz(kl);
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = -mref;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int dc = 2 * s + half;
-        const bf16x8 kfrag = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ((dc ^ sw) * 8)));
-        sacc[kb] = mfma32(kfrag, qf[s], sacc[kb]);
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf =
+            as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[s] + kb * 32 * D));
+        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
       }
     }
 
-    // ---- mask the keys past the window end (last tile only) ----
-    if (j * kBN + kBN > nk) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -228,17 +276,32 @@ window_attn_kernel(AttnArgs a) {
         }
     }
 
-    // ---- online softmax (base 2) ----
+    // ---- tile max relative to the reference; move it if needed ----
     float tmax = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 1; r < 15; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[0][r]), sacc[0][r + 1]);
+    tmax = fmaxf(fmaxf(tmax, sacc[0][15]), sacc[1][0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
+    for (int r = 1; r < 15; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[1][r]), sacc[1][r + 1]);
+    tmax = fmaxf(tmax, sacc[1][15]);
     tmax = pair_max(tmax);
-    const float mnew = fmaxf(mrow, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
-    mrow = mnew;
-    float psum = 0.f;
+    const bool need = (j == 0) || (tmax > kRescale);
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float shift = need ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      mref += shift;
+      lrow *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
+    }
+
+    // ---- probabilities (bf16) and their sum ----
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -247,35 +310,48 @@ window_attn_kernel(AttnArgs a) {
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e] - mnew);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e + 1] - mnew);
-          psum += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
+          bf16x2 pp;
+          pp[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e]);
+          pp[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e + 1]);
+          lrow = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lrow, false);
+          pk[e] = __builtin_bit_cast(uint32_t, pp);
         }
         pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
       }
-    lrow = lrow * alpha + psum;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int kc = 4 * kb + 2 * g + half;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const int d = 32 * b + l32;
-          const bf16x8 vfrag =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&lds_v[buf][d * kBN + ((kc ^ (d & 7)) * 8)]));
-          oacc[b] = mfma32(vfrag, pf[kb][g], oacc[b]);
+          // key chunk 4 kb + 2 g + half of dim 32 b + l32
+          const bf16x8 vf = as_bf16x8(
+              *reinterpret_cast<const uint4*>(V + voffr[2 * kb + g] + b * 32 * kBN));
+          oacc[b] = mfma32(vf, pf[kb][g], oacc[b]);
         }
       }
+  };
 
-    if (more) lstore(buf ^ 1);
+  // unrolled by two so that the LDS buffer of each tile is a compile-time
+  // constant (folded into the ds_read offsets)
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const bool last_partial = ntiles * kBN > nk;
+  const int nfull = last_partial ? ntiles - 1 : ntiles;
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    tile(j, std::false_type{}, B0{});
+    tile(j + 1, std::false_type{}, B1{});
+  }
+  if (j < nfull) {
+    tile(j, std::false_type{}, B0{});
+    ++j;
+  }
+  if (last_partial) {
+    if (j & 1) tile(j, std::true_type{}, B1{});
+    else tile(j, std::true_type{}, B0{});
   }
 
   // ---- epilogue: normalise, store bf16 O and the log-sum-exp ----
@@ -294,7 +370,7 @@ window_attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint2*>(op + d) = v;
       }
     if (a.lse && half == 0)
-      a.lse[int64_t(h) * a.NQ + qn] = (mrow + __builtin_log2f(ltot)) * 0.6931471805599453f;
+      a.lse[int64_t(h) * a.NQ + qn] = (mref + __builtin_log2f(ltot)) * 0.6931471805599453f;
   }
 }
 
