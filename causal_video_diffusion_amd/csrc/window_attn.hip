@@ -4,9 +4,14 @@
 // load (abstract: fused RoPE with cached coefficients).
 //
 // Design (gfx950, wave64, bf16 MFMA 32x32x16 with fp32 accumulation):
-//  * A workgroup of 4 waves owns 128 queries of one head; each wave owns 32.
-//    Two workgroups share a CU (2 waves per SIMD), so one wave's softmax
-//    VALU work overlaps the other's MFMA work.
+//  * One workgroup of 8 waves per CU owns 256 queries of one head (32 per
+//    wave), so every K/V tile brought into LDS feeds 256 queries.  Waves w
+//    and w+4 share a SIMD.  The two groups (waves 0-3, 4-7) run a phase
+//    apart ("ping-pong"): in every phase one group issues MFMAs (PV of the
+//    previous tile, then QK of the current one) while the other computes the
+//    softmax of its current tile, so on each SIMD one wave's VALU work runs
+//    under the other wave's matrix work.  A workgroup barrier separates the
+//    phases.
 //  * The window's keys form one virtual sequence (frame after frame, each
 //    frame's T keys read from its ring slot), walked in tiles of 64 keys;
 //    only the last tile can be partial, and a tile may straddle frames.
@@ -24,13 +29,16 @@
 //    swapped) so that each lane's 8 score registers of one 16-key group hold
 //    8 consecutive keys: those registers, rounded to bf16, are directly the
 //    B operand of O^T = V^T P^T.  V^T comes from the transposed value cache,
-//    so neither P nor V is transposed on chip.  The row sum is accumulated
-//    from the same bf16 pairs with v_dot2_f32_bf16.
+//    so neither P nor V is transposed on chip.  The row sum uses plain fp32
+//    adds: on gfx950 dot-product instructions share the matrix pipe and
+//    would stall behind the partner wave's MFMAs.
 //  * K and V^T tiles go straight from global memory to LDS
-//    (global_load_lds_dwordx4, no register staging), double-buffered, with
-//    16-byte chunks XOR-swizzled so that every 16-lane group of an MFMA
-//    operand read touches 64 distinct banks.  Tiles inside one frame use a
-//    uniform base address plus per-lane constant offsets.
+//    (global_load_lds_dwordx4, no register staging) through a 4-stage ring:
+//    tile t+2 is requested while tile t is consumed, so each load has four
+//    phases to land.  16-byte chunks are XOR-swizzled so that every 16-lane
+//    group of an MFMA operand read touches 64 distinct banks.  The loop is
+//    unrolled over the 4 stages so every LDS address is a register plus an
+//    immediate.
 //  * Workgroups are numbered so that each XCD (8 per chip, dispatched round
 //    robin) gets a contiguous run of (head, query tile) work: the workgroups
 //    streaming one head's K/V share an L2.
@@ -43,12 +51,11 @@
 namespace ust {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kStages = 4;     // LDS ring of K/V tiles
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr float kRescale = 8.0f;  // move the reference max when exceeded (log2 units)
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // swap bits 2 and 3 of a row index within a 32-row MFMA block
 __device__ __forceinline__ int perm_row(int i) {
@@ -85,12 +92,50 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
 }
 
-__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* l) {
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (lds_void*)(l), 16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane
+// (global_load_lds_dwordx4).  Issued from inline asm so that the compiler
+// does not track the LDS write: it would otherwise wait for every such load
+// before any later LDS read.  Ordering is explicit instead: each wave waits
+// for its own loads (vmcnt) before the workgroup barrier that precedes the
+// first read of the stage, and a stage is only rewritten after the barrier
+// that follows its last read.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
+}
+__device__ __forceinline__ void load_lds16(const uint16_t* g, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0));
+}
+__device__ __forceinline__ void load_lds16_s(const uint16_t* sbase, uint32_t voff_bytes, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(sbase), "{m0}"(m0));
+}
+
+// s_waitcnt with vmcnt <= N and the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier that neither waits for outstanding loads nor lets the
+// compiler move memory accesses across it
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Order N (LDS read, MFMA) pairs as: kPre reads, then alternately one MFMA
+// and one read, then the last kPre MFMAs, so every MFMA finds its operand
+// read kPre MFMAs earlier.
+constexpr int kPre = 4;
+template <int N>
+__device__ __forceinline__ void sched_pipeline() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kPre, 0);
+#pragma unroll
+  for (int i = 0; i < N - kPre; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, kPre, 0);
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 window_attn_kernel(AttnArgs a) {
   constexpr int KS = D / 16;                          // k-steps of the score product
   constexpr int DB = D / 32;                          // 32-row blocks of O^T
@@ -98,8 +143,26 @@ window_attn_kernel(AttnArgs a) {
   constexpr int KRPI = 64 / KCPR;                     // key rows per 1 KB load
   constexpr int KINST = kBN * D * 2 / 1024 / kWaves;  // K loads per wave per tile
   constexpr int VINST = D * kBN * 2 / 1024 / kWaves;  // V^T loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][D * kBN];
+  constexpr int NLD = KINST + VINST;                  // loads per wave per tile
+  // one array per stage, so that alias analysis can tell a stage being read
+  // from the stages the tile loads are writing (no needless waits)
+  __shared__ __attribute__((aligned(1024))) uint16_t lk0[kBN * D], lk1[kBN * D], lk2[kBN * D], lk3[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv0[D * kBN], lv1[D * kBN], lv2[D * kBN], lv3[D * kBN];
+  static_assert(kStages == 4, "one LDS array per stage");
+  auto kstage = [&](auto tag) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int b = decltype(tag)::value;
+    if constexpr (b == 0) return lk0;
+    else if constexpr (b == 1) return lk1;
+    else if constexpr (b == 2) return lk2;
+    else return lk3;
+  };
+  auto vstage = [&](auto tag) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int b = decltype(tag)::value;
+    if constexpr (b == 0) return lv0;
+    else if constexpr (b == 1) return lv1;
+    else if constexpr (b == 2) return lv2;
+    else return lv3;
+  };
   __shared__ uint32_t kbase[UST_MAX_WINDOW_FRAMES];
   __shared__ uint32_t vbase[UST_MAX_WINDOW_FRAMES];
 
@@ -110,6 +173,7 @@ window_attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_a = wave < 4;   // waves w and w + 4 share a SIMD
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int T = a.T;
@@ -117,7 +181,7 @@ window_attn_kernel(AttnArgs a) {
   const int nk = a.n_frames * T;
   const int ntiles = (nk + kBN - 1) / kBN;
 
-  for (int i = tid; i < a.n_frames; i += 256) {
+  for (int i = tid; i < a.n_frames; i += 512) {
     kbase[i] = uint32_t((a.slots[i] * a.H + h) * T * D);
     vbase[i] = uint32_t((a.slots[i] * a.H + h) * D * TV);
   }
@@ -155,57 +219,83 @@ window_attn_kernel(AttnArgs a) {
   __syncthreads();  // kbase / vbase visible
 
   // ---- per-lane constants of the tile loads ----
-  // K load i of this wave fills LDS bytes [(wave*KINST + i) KB, +1 KB): key row
-  // krow[i], 16-byte chunk kdc[i] (logical; stored at the lane's position).
-  int krow[KINST], koff[KINST];
+  // K load i of wave w fills LDS bytes [(w*KINST + i) KB, +1 KB): key row
+  // `row`, logical 16-byte chunk (stored at this lane's position).
+  int koff[KINST], voff[VINST];
 #pragma unroll
   for (int i = 0; i < KINST; ++i) {
     const int row = KRPI * (wave * KINST + i) + lane / KCPR;
-    const int dc = (lane % KCPR) ^ kswz<D>(row);
-    krow[i] = row;
-    koff[i] = row * D + dc * 8;
+    koff[i] = row * D + (((lane % KCPR) ^ kswz<D>(row)) * 8);
   }
-  // V^T load i: dimension vd[i], 8-key chunk vkc[i]
-  int vd[VINST], vkc[VINST], voff[VINST];
 #pragma unroll
   for (int i = 0; i < VINST; ++i) {
     const int d = 8 * (wave * VINST + i) + lane / 8;
-    const int kc = (lane % 8) ^ vswz(d);
-    vd[i] = d;
-    vkc[i] = kc;
-    voff[i] = d * TV + kc * 8;
+    voff[i] = d * TV + (((lane % 8) ^ vswz(d)) * 8);
   }
 
-  // Issue the global->LDS loads of tile (fi, t0) into buffer buf.
-  auto issue = [&](int j, int fi, int t0, int buf) {
-    uint16_t* lk = &lds_k[buf][wave * KINST * 512];
-    uint16_t* lv = &lds_v[buf][wave * VINST * 512];
-    if (t0 + kBN <= T && j * kBN + kBN <= nk) {
-      // whole tile inside frame fi: uniform base + lane constants
-      const uint16_t* kb = a.k_cache + kbase[fi] + uint32_t(t0 * D);
-      const uint16_t* vb = a.v_cache + vbase[fi] + uint32_t(t0);
+  // Element offsets of this lane's MFMA operand fragments within a tile
+  // buffer.  Key block kb adds 32 rows (kswz is the same for rows r and
+  // r + 32) and O^T block b adds 32 dims (vswz likewise), so those and the
+  // buffer index fold into the ds_read immediate offsets.
+  int koffr[KS], voffr[4];
+  {
+    const int row = perm_row(l32);
 #pragma unroll
-      for (int i = 0; i < KINST; ++i) load_lds16(kb + koff[i], lk + i * 512);
+    for (int s = 0; s < KS; ++s) koffr[s] = row * D + (((2 * s + half) ^ kswz<D>(row)) * 8);
 #pragma unroll
-      for (int i = 0; i < VINST; ++i) load_lds16(vb + voff[i], lv + i * 512);
+    for (int q = 0; q < 4; ++q) voffr[q] = l32 * kBN + (((2 * q + half) ^ vswz(l32)) * 8);
+  }
+
+  // Issue the global->LDS loads of tile t (starting at frame lfi, token lt0).
+  // kfb / vfb: the frame's key and value slot bases (wave-uniform), reloaded
+  // only when the load position moves to the next frame.
+  int lfi = 0, lt0 = 0;   // position of the next tile to load
+  const uint16_t* kfb = a.k_cache + (int64_t(a.slots[0]) * a.H + h) * T * D;
+  const uint16_t* vfb = a.v_cache + (int64_t(a.slots[0]) * a.H + h) * D * TV;
+  auto next_frame = [&]() __attribute__((always_inline)) {
+    ++lfi;
+    if (lfi < a.n_frames) {
+      kfb = a.k_cache + (int64_t(a.slots[lfi]) * a.H + h) * T * D;
+      vfb = a.v_cache + (int64_t(a.slots[lfi]) * a.H + h) * D * TV;
+    }
+  };
+  auto issue = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+    const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr(kstage(buf_tag) + wave * KINST * 512));
+    const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(vstage(buf_tag) + wave * VINST * 512));
+    if (lt0 + kBN <= T && t * kBN + kBN <= nk) {
+      // whole tile inside one frame: uniform base + lane constants
+      const uint16_t* kb = kfb + lt0 * D;
+      const uint16_t* vb = vfb + lt0;
+#pragma unroll
+      for (int i = 0; i < KINST; ++i) load_lds16_s(kb, uint32_t(koff[i]) * 2u, lk + i * 1024);
+#pragma unroll
+      for (int i = 0; i < VINST; ++i) load_lds16_s(vb, uint32_t(voff[i]) * 2u, lv + i * 1024);
     } else {
       // straddles frames or runs past the window: per-lane frame lookup;
       // keys past the window are pointed at the window's first key (finite
       // data whose probability is masked to zero)
 #pragma unroll
       for (int i = 0; i < KINST; ++i) {
-        int tt = t0 + krow[i], f = fi;
+        const int row = KRPI * (wave * KINST + i) + lane / KCPR;
+        int tt = lt0 + row, f = lfi;
         while (tt >= T) { tt -= T; ++f; }
         if (f >= a.n_frames) { f = 0; tt = 0; }
-        load_lds16(a.k_cache + kbase[f] + uint32_t(tt * D) + (koff[i] - krow[i] * D), lk + i * 512);
+        load_lds16(a.k_cache + kbase[f] + uint32_t(tt * D) + (koff[i] - row * D), lk + i * 1024);
       }
 #pragma unroll
       for (int i = 0; i < VINST; ++i) {
-        int tt = t0 + 8 * vkc[i], f = fi;
+        const int d = 8 * (wave * VINST + i) + lane / 8;
+        const int kc = (lane % 8) ^ vswz(d);
+        int tt = lt0 + 8 * kc, f = lfi;
         while (tt >= T) { tt -= T; ++f; }
         if (f >= a.n_frames) { f = 0; tt = 0; }
-        load_lds16(a.v_cache + vbase[f] + uint32_t(tt) + uint32_t(vd[i] * TV), lv + i * 512);
+        load_lds16(a.v_cache + vbase[f] + uint32_t(tt) + uint32_t(d * TV), lv + i * 1024);
       }
+    }
+    lt0 += kBN;
+    while (lt0 >= T) {
+      lt0 -= T;
+      next_frame();
     }
   };
 
@@ -216,76 +306,67 @@ window_attn_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float mref = 0.f;   // reference max (log2 units) of this lane's query
   float lrow = 0.f;   // this lane's share of the running sum, relative to mref
+  f32x16 sacc[2];     // S^T - mref of the tile being computed
+  bf16x8 pf[2][2];    // bf16 probabilities of the tile awaiting PV
 
-  int fi = 0, t0 = 0;           // frame index and token of the next tile to load
-  issue(0, fi, t0, 0);
-  t0 += kBN;
-  while (t0 >= T) { t0 -= T; ++fi; }
-
-  // Element offsets of this lane's MFMA operand fragments within a tile
-  // buffer (fixed across tiles).  Key block kb adds 32 rows (kswz is the same
-  // for rows r and r + 32) and O^T block b adds 32 dims (vswz likewise), so
-  // those and the buffer index fold into the ds_read immediate offsets.
-  int koffr[KS], voffr[4];
-  {
-    const int row = perm_row(l32);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) koffr[s] = row * D + (((2 * s + half) ^ kswz<D>(row)) * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) voffr[q] = l32 * kBN + (((2 * q + half) ^ vswz(l32)) * 8);
-  }
-
-  // One tile: scores, online softmax, PV.  MASKED is the last tile, whose
-  // keys past the window end get probability zero.
-  auto tile = [&](int j, auto masked_tag, auto buf_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int buf = decltype(buf_tag)::value;   // == j & 1
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile j are in LDS
-    __syncthreads();                 // ... and every wave's; buf^1 is free
-    if (!MASKED && j + 1 < ntiles) {
-      issue(j + 1, fi, t0, buf ^ 1);
-      t0 += kBN;
-      while (t0 >= T) { t0 -= T; ++fi; }
-    }
-    const uint16_t* K = lds_k[buf];
-    const uint16_t* V = lds_v[buf];
-
-    // ---- S^T - mref = K Q^T + (-mref), two 32-key blocks ----
-    f32x16 sacc[2];
+  // ---- S^T - mref = K Q^T + (-mref), two 32-key blocks ----
+  // The fragment reads run kPre ahead of the MFMAs that consume them (the
+  // scheduling-group barriers pin that order), so the MFMA pipe does not
+  // wait on LDS latency.
+  auto qk = [&](auto buf_tag) __attribute__((always_inline)) {
+    const uint16_t* K = kstage(buf_tag);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = -mref;
+    bf16x8 kf[2 * KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int i = 0; i < 2 * KS; ++i)
+      kf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[i >> 1] + (i & 1) * 32 * D));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf =
-            as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[s] + kb * 32 * D));
-        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-      }
-    }
+    for (int i = 0; i < 2 * KS; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
+    sched_pipeline<2 * KS>();
+  };
 
-    if constexpr (MASKED) {
+  // ---- O^T += V^T P^T ----
+  auto pv = [&](auto buf_tag) __attribute__((always_inline)) {
+    const uint16_t* V = vstage(buf_tag);
+    // fragment i: key chunk 4 kb + 2 g + half of dim 32 b + l32, with
+    // q = 2 kb + g = i / DB, b = i % DB
+    bf16x8 vf[4 * DB];
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i)
+      vf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(V + voffr[i / DB] + (i % DB) * 32 * kBN));
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i)
+      oacc[i % DB] = mfma32(vf[i], pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
+    sched_pipeline<4 * DB>();
+  };
+
+  // ---- online softmax of tile t: bf16 probabilities into pf ----
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    if (t == ntiles - 1 && ntiles * kBN > nk) {
+      asm volatile("; last tile: keys past the window end");
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * kBN + 32 * kb + 16 * (r / 8) + 8 * half + (r % 8);
+          const int key = t * kBN + 32 * kb + 16 * (r / 8) + 8 * half + (r % 8);
           if (key >= nk) sacc[kb][r] = -INFINITY;
         }
     }
-
-    // ---- tile max relative to the reference; move it if needed ----
-    float tmax = sacc[0][0];
+    // tile max: a tree of independent max3 ops, not one long dependent chain
+    float m4[4];
 #pragma unroll
-    for (int r = 1; r < 15; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[0][r]), sacc[0][r + 1]);
-    tmax = fmaxf(fmaxf(tmax, sacc[0][15]), sacc[1][0]);
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[1][r]), sacc[1][r + 1]);
-    tmax = fmaxf(tmax, sacc[1][15]);
+    for (int c = 0; c < 4; ++c) {
+      const int kb = c >> 1, r0 = 8 * (c & 1);
+      m4[c] = fmaxf(fmaxf(fmaxf(sacc[kb][r0], sacc[kb][r0 + 1]), sacc[kb][r0 + 2]),
+                    fmaxf(fmaxf(sacc[kb][r0 + 3], sacc[kb][r0 + 4]),
+                          fmaxf(fmaxf(sacc[kb][r0 + 5], sacc[kb][r0 + 6]), sacc[kb][r0 + 7])));
+    }
+    float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     tmax = pair_max(tmax);
-    const bool need = (j == 0) || (tmax > kRescale);
+    const bool need = (t == 0) || (tmax > kRescale);
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float shift = need ? tmax : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-shift);
@@ -300,59 +381,77 @@ window_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
     }
-
-    // ---- probabilities (bf16) and their sum ----
-    bf16x8 pf[2][2];
+    // probabilities in place (32 independent exp2), the row sum in fp32 in
+    // four independent partial sums (plain adds: dot-product instructions
+    // would contend with the partner wave's MFMAs), then bf16 pairs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls[r & 3] += sacc[kb][r];
+    lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16x2 pp;
-          pp[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e]);
-          pp[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][8 * g + 2 * e + 1]);
-          lrow = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lrow, false);
-          pk[e] = __builtin_bit_cast(uint32_t, pp);
-        }
+        for (int e = 0; e < 4; ++e)
+          pk[e] = pack_bf16x2(sacc[kb][8 * g + 2 * e], sacc[kb][8 * g + 2 * e + 1]);
         pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-      }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          // key chunk 4 kb + 2 g + half of dim 32 b + l32
-          const bf16x8 vf = as_bf16x8(
-              *reinterpret_cast<const uint4*>(V + voffr[2 * kb + g] + b * 32 * kBN));
-          oacc[b] = mfma32(vf, pf[kb][g], oacc[b]);
-        }
       }
   };
 
-  // unrolled by two so that the LDS buffer of each tile is a compile-time
-  // constant (folded into the ds_read offsets)
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  const bool last_partial = ntiles * kBN > nk;
-  const int nfull = last_partial ? ntiles - 1 : ntiles;
-  int j = 0;
-  for (; j + 1 < nfull; j += 2) {
-    tile(j, std::false_type{}, B0{});
-    tile(j + 1, std::false_type{}, B1{});
+  // ---- the phase schedule ----
+  // Every wave runs the same sequence; group B starts one barrier later, so
+  // its phases are offset by one from group A's:
+  //   MFMA phase t:    QK(t); PV(t-1); barrier
+  //   softmax phase t: request own share of tile t+L; softmax(t); wait for own
+  //                    share of tile t+L-1; barrier
+  // with L = 2 for group A and L = 3 for group B, so every share of tile u is
+  // in LDS before group A's MFMA phase u, and the loads and their waits sit in
+  // softmax phases, under the partner wave's MFMA phase.  Tile u lives in LDS
+  // stage u % 4 from its first request (group B's softmax phase u-3) until
+  // group B's PV(u) (its MFMA phase u+1).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  const int lead = group_a ? 2 : 3;
+  auto step = [&](int t, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    if (t < ntiles) qk(cur);     // first, so its scores are ready for softmax(t)
+    if (t >= 1) pv(prev);
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    const int u = t + lead;      // tile this wave requests now
+    if (u < ntiles) {
+      if (group_a) issue(u, st2);
+      else issue(u, st3);
+    }
+    if (t < ntiles) softmax(t);
+    if (u < ntiles) wait_vmcnt<NLD>();   // own share of tile u-1 landed
+    else wait_vmcnt<0>();
+    barrier();
+  };
+
+  issue(0, S0{});
+  if (ntiles > 1) issue(1, S1{});
+  if (!group_a && ntiles > 2) issue(2, S2{});
+  wait_vmcnt<0>();
+  barrier();                        // tiles 0 .. lead-1 are in LDS
+  if (!group_a) barrier();          // group B runs one phase behind
+  for (int t = 0; t <= ntiles; t += 4) {
+    step(t, S0{}, S3{}, S2{}, S3{});
+    if (t + 1 <= ntiles) step(t + 1, S1{}, S0{}, S3{}, S0{});
+    if (t + 2 <= ntiles) step(t + 2, S2{}, S1{}, S0{}, S1{});
+    if (t + 3 <= ntiles) step(t + 3, S3{}, S2{}, S1{}, S2{});
   }
-  if (j < nfull) {
-    tile(j, std::false_type{}, B0{});
-    ++j;
-  }
-  if (last_partial) {
-    if (j & 1) tile(j, std::true_type{}, B1{});
-    else tile(j, std::true_type{}, B0{});
-  }
+  if (group_a) barrier();           // match group B's extra barrier
 
   // ---- epilogue: normalise, store bf16 O and the log-sum-exp ----
   const float ltot = pair_sum(lrow);
@@ -380,9 +479,9 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
   const int nqt = (a.NQ + kBM - 1) / kBM;
   dim3 grid(nqt * a.H);
   if (a.D == 128)
-    hipLaunchKernelGGL(window_attn_kernel<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<128>, grid, dim3(64 * kWaves), 0, s, a);
   else
-    hipLaunchKernelGGL(window_attn_kernel<64>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<64>, grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
