@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1560,
                     help="query rows of the oracle's sample (of 4680)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB "
+                         "(a known-size reference for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -113,6 +116,14 @@ def main():
         P.lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
         if ev is not None:
             ev[4].record(stream)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
