@@ -321,3 +321,75 @@ def test_layer_chunk_wan_window_chained():
         y_ref = O.lowrank_proj(o_ref.reshape(len(rows), -1), _f64(ao), _f64(bo))
         print(f"[layer_chunk wan_window chunk {c}]", flush=True)
         assert_close(_f64(P.from_device_bf16(y))[rows], y_ref, f"chunk {c} Y")
+
+
+# ------------------------------------------------------------------ clip schedule
+
+@pytest.mark.timeout(600)
+def test_clip_schedule_wan_clip():
+    """The 81-frame clip over 30 layers (UnStep, Table 3: 4 forwards for the
+    first chunk, 2 for each later one, plus a clean-cache forward per chunk).
+    Every forward of a chunk writes the chunk's frames; every layer has its
+    own weights and ring and sees the same hidden states (reading).  The GPU
+    runs all 23 x 30 layer-chunks; sampled (layer, forward, rows) are checked
+    against the oracle, which rebuilds the cache state the sample sees: the
+    clean-cache forward's keys/values for earlier chunks, the forward's own
+    for the current chunk."""
+    w = wl.WAN_CLIP
+    g = _g(w)
+    sched = P.clip_forwards(w.n_chunks, w.first_steps, w.later_steps, w.clean_pass)
+    assert len(sched) == 23
+    assert [f for f in sched] == O.clip_schedule(w.n_chunks, w.first_steps,
+                                                 w.later_steps, w.clean_pass)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    samples = {(0, 0), (17, 12), (29, 22), (8, 5)}      # (layer, forward index)
+    print("[clip: preparing 30 layers of weights]", flush=True)
+    layers = []
+    for layer in range(w.layers):
+        wq = wl.dense_weight_bf16(w, wl.TAG_WQ, layer)
+        wk = wl.dense_weight_bf16(w, wl.TAG_WK, layer)
+        av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank, layer)
+        ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, w.rank, layer)
+        layers.append(dict(
+            wq=P.LowRank(P.to_device_bf16(P.output_major(wq)), None),
+            wk=P.LowRank(P.to_device_bf16(P.output_major(wk)), None),
+            wv=P.LowRank.from_bits(av, bv), wo=P.LowRank.from_bits(ao, bo),
+            ring=P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS),
+            host=(wq, wk, av, bv, ao, bo)))
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank)
+    qbuf = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    kbuf = torch.empty_like(qbuf)
+    got = {}
+    print("[clip: running 23 forwards x 30 layers]", flush=True)
+    for fi, (c, s, clean) in enumerate(sched):
+        x = P.to_device_bf16(wl.activations(w, c, s))
+        for layer, L in enumerate(layers):
+            P.lowrank_apply(L["wq"], x, qbuf)
+            P.lowrank_apply(L["wk"], x, kbuf)
+            y = P.layer_chunk(g, L["ring"], table, x, qbuf, kbuf, L["wv"], L["wo"], 3 * c,
+                              w.n_recent, bufs)
+            if (layer, fi) in samples:
+                got[(layer, fi)] = P.from_device_bf16(y)
+    torch.cuda.synchronize()
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    last_forward = {c: max(i for i, f in enumerate(sched) if f[0] == c) for c in range(w.n_chunks)}
+    for (layer, fi) in sorted(samples):
+        c, s, clean = sched[fi]
+        wq, wk, av, bv, ao, bo = (_f64(a) for a in layers[layer]["host"])
+        cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+        frames, _ = O.window_slots(3 * c, 3, w.n_sink, w.n_recent, w.n_slots)
+        for cc in sorted({f // 3 for f in frames}):
+            step_cc = s if cc == c else sched[last_forward[cc]][1]
+            xcc = _f64(wl.activations(w, cc, step_cc))
+            k = (xcc @ wk).reshape(w.n_q, w.n_heads, -1)
+            v = O.lowrank_proj(xcc, av, bv).reshape(w.n_q, w.n_heads, -1)
+            O.kv_append(cache, k, v, cos, sin, 3 * cc, 3, w.grid_h, w.grid_w, w.n_slots, w.n_sink)
+        rows = _sample_rows(w.n_q, 128, seed=fi)
+        xq = _f64(wl.activations(w, c, s))[rows]
+        q = np.zeros((w.n_q, w.n_heads, w.head_dim))
+        q[rows] = (xq @ wq).reshape(len(rows), w.n_heads, -1)
+        o_ref, _ = O.window_attn(cache, q, cos, sin, 3 * c, 3, w.grid_h, w.grid_w, w.n_slots,
+                                 w.n_sink, w.n_recent, rows=rows)
+        y_ref = O.lowrank_proj(o_ref.reshape(len(rows), -1), ao, bo)
+        print(f"[clip layer {layer} forward {fi} (chunk {c}, step {s}, clean {clean})]", flush=True)
+        assert_close(_f64(got[(layer, fi)])[rows], y_ref, f"clip layer {layer} forward {fi}")
