@@ -10,6 +10,10 @@
 //    both operand tiles k-contiguous in LDS with an XOR swizzle on 16-byte
 //    chunks (conflict-free MFMA operand reads), double-buffered.
 //  * Ragged M, N and K are zero-filled at the tile loads; stores are masked.
+//  * When K is a multiple of 64 a pipelined variant (below) streams tiles
+//    straight into LDS instead of through registers.
+
+#include <type_traits>
 
 #include "ust_device.h"
 #include "ust_internal.h"
@@ -135,9 +139,242 @@ gemm_nt_kernel(GemmArgs g) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Pipelined variant for K % 64 == 0.  Tiles go global -> LDS by
+// global_load_lds_dwordx4 (issued from inline asm, so the compiler adds no
+// waits for them) through a ring of STAGES k-slices; the loads of slice
+// kt + STAGES - 1 are issued at step kt.  Each wave waits for its own loads
+// of slice kt (vmcnt) and its own LDS reads of slice kt - 1 (lgkmcnt) before
+// the barrier that opens step kt, so after that barrier slice kt is complete
+// and the stage slice kt - 1 used is free to be refilled.  Rows past M or N
+// load clamped (finite) rows whose results are never stored.
+//
+// Tiles are BM x BN with 4 waves in a 2 x 2 grid; the launcher picks the
+// shape so that one round of workgroups (one per CU) covers the output.  The
+// workgroup -> tile map is XCD-aware: workgroups are dealt to the 8 XCDs
+// round-robin, and each XCD gets a contiguous, row-major run of tiles, so the
+// tiles that share rows of X run on one XCD and find them in its L2.
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
+}
+__device__ __forceinline__ void load_lds16_s(const uint16_t* sbase, uint32_t voff_bytes, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(sbase), "{m0}"(m0));
+}
+// wait until at most N vector-memory ops of this wave are in flight and all
+// of its LDS reads have returned (so the next barrier orders them too)
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }  // 128-byte rows
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int BM, int BN, int STAGES>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_nt_dma_kernel(GemmArgs g) {
+  constexpr int MB = BM / 64;              // 32-row blocks of X per wave
+  constexpr int NB = BN / 64;              // 32-row blocks of W per wave
+  constexpr int FR = NB + MB;              // fragments per 16-wide k substep
+  constexpr int NMMA = NB * MB;            // MFMAs per substep
+  constexpr int XI = BM / 8, WI = BN / 8;  // 1 KB loads per slice for X and W
+  constexpr int NLD = (XI + WI) / 4;       // loads per wave per slice
+  static_assert((XI + WI) % 4 == 0, "loads split evenly over 4 waves");
+  constexpr int STAGE = (BM + BN) * 64;    // elements per stage: X rows, then W rows
+  constexpr int LA = STAGES - 1;           // slices in flight beyond the current one
+  static_assert(STAGES >= 2 && STAGES <= 4, "the vmcnt cases below cover 1 to 3 slices");
+  constexpr int ES = BN + 8;               // epilogue staging row stride (elements)
+  static_assert(BM * ES <= STAGES * STAGE, "epilogue tile fits in the ring");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nbn = (g.N + BN - 1) / BN;
+  const int ntile = ((g.M + BM - 1) / BM) * nbn;
+  const int xcd = blockIdx.x & 7, q = ntile >> 3, r = ntile & 7;
+  const int tile = xcd * q + min(xcd, r) + (blockIdx.x >> 3);
+  const int m0 = (tile / nbn) * BM;
+  const int n0 = (tile % nbn) * BN;
+  const int nkt = g.K / 64;
+
+  // per-lane byte offsets of this wave's loads; 8 lanes fill one 128-byte
+  // stage row, with the row's 16-byte chunks XOR-swizzled
+  uint32_t voff[NLD];
+  bool isx[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int gi = wave * NLD + i;
+    const int row = 8 * gi + lane / 8;
+    const int c = (lane % 8) ^ swz(row);
+    isx[i] = gi < XI;
+    const int rr = isx[i] ? min(m0 + row, g.M - 1) : min(n0 + row - BM, g.N - 1);
+    voff[i] = uint32_t(rr * g.K + c * 8) * 2u;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * NLD * 1024;
+  // load i (of NLD) of slice kt into stage st
+  auto dma = [&](int kt, int st, int i) __attribute__((always_inline)) {
+    load_lds16_s(isx[i] ? g.x + kt * 64 : g.w + kt * 64, voff[i],
+                 lds0 + st * STAGE * 2 + i * 1024);
+  };
+
+  // fragment f of substep s: f < NB is W block f, else X block f - NB
+  int offr[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = (2 * s + half) ^ swz(l32);
+    offr[s][0] = (BM + wn * 32 * NB + l32) * 64 + c * 8;
+    offr[s][1] = (wm * 32 * MB + l32) * 64 + c * 8;
+  }
+  bf16x8 fr[4][FR];
+  auto rd = [&](const uint16_t* L, int s, int f) __attribute__((always_inline)) {
+    const int o = f < NB ? offr[s][0] + f * 32 * 64 : offr[s][1] + (f - NB) * 32 * 64;
+    fr[s][f] = as_bf16x8(*reinterpret_cast<const uint4*>(L + o));
+  };
+
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mma = [&](int s, int idx) __attribute__((always_inline)) {
+    const int i = idx / MB, j = idx % MB;
+    acc[i][j] = mfma32(fr[s][i], fr[s][NB + j], acc[i][j]);
+  };
+
+  // One half-slice phase: the MFMAs of substeps s0, s0 + 1 of the current
+  // slice, interleaved with the reads of substeps rs0, rs0 + 1 from stage
+  // RL and, when do_dma, with loads [d0, d1) of slice du into stage dst.
+  // The loads sit behind uniform branches that also pin the MFMA order; the
+  // MFMAs themselves are on the one path every wave takes.
+  auto phase = [&](int s0, const uint16_t* RL, int rs0, bool do_dma, int du, int dst, auto d0c,
+                   auto d1c) __attribute__((always_inline)) {
+    constexpr int d0 = decltype(d0c)::value, d1 = decltype(d1c)::value;
+    constexpr int NM = 2 * NMMA, NR = 2 * FR, ND = d1 - d0;
+    static_for<0, NM>([&](auto qc) {
+      constexpr int qi = decltype(qc)::value;
+      static_for<qi * NR / NM, (qi + 1) * NR / NM>([&](auto rc) {
+        constexpr int ri = decltype(rc)::value;
+        rd(RL, rs0 + ri / FR, ri % FR);
+      });
+      if constexpr ((qi + 1) * ND / NM > qi * ND / NM) {
+        if (do_dma) {
+          static_for<qi * ND / NM, (qi + 1) * ND / NM>([&](auto dc) {
+            dma(du, dst, d0 + decltype(dc)::value);
+          });
+        }
+      }
+      mma(s0 + qi / NMMA, qi % NMMA);
+    });
+  };
+  using Z = std::integral_constant<int, 0>;
+  using H = std::integral_constant<int, NLD / 2>;
+  using F = std::integral_constant<int, NLD>;
+
+  // wait for slice j (with `ahead` later slices possibly in flight) and for
+  // this wave's LDS reads, then the barrier that publishes slice j
+  auto sync_slice = [&](int ahead) __attribute__((always_inline)) {
+    if (ahead >= LA - 1) wait_vm_lds<(LA - 1) * NLD>();
+    else if (LA >= 3 && ahead == 1) wait_vm_lds<NLD>();
+    else wait_vm_lds<0>();
+    barrier();
+  };
+
+  // prologue: slices 0 .. LA-1, then slice 0 published, first half of
+  // slice LA requested and the first two substeps of slice 0 read
+  static_for<0, LA>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (i < nkt) static_for<0, NLD>([&](auto dc) { dma(i, i, decltype(dc)::value); });
+  });
+  sync_slice(nkt - 1);
+  if (LA < nkt) static_for<0, NLD / 2>([&](auto dc) { dma(LA, LA % STAGES, decltype(dc)::value); });
+#pragma unroll
+  for (int f = 0; f < FR; ++f) rd(lds, 0, f);
+#pragma unroll
+  for (int f = 0; f < FR; ++f) rd(lds, 1, f);
+
+  // slice kt lives in stage st = kt % STAGES; after the last slice the
+  // phase-B reads fetch a stale stage whose fragments go unused
+  int st = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int stn = st + 1 == STAGES ? 0 : st + 1;
+    const int stl = st == 0 ? STAGES - 1 : st - 1;  // stage of slice kt + LA
+    // A: substeps 0, 1; read substeps 2, 3; second half of slice kt + LA
+    phase(0, lds + st * STAGE, 2, kt + LA < nkt, kt + LA, stl, H{}, F{});
+    if (kt + 1 < nkt) sync_slice(nkt - 2 - kt);
+    // B: substeps 2, 3; read substeps 0, 1 of slice kt + 1; first half of
+    // slice kt + 1 + LA into the stage slice kt has just left
+    phase(2, lds + stn * STAGE, 0, kt + 1 + LA < nkt, kt + 1 + LA, st, Z{}, H{});
+    st = stn;
+  }
+
+  // epilogue: bias, bf16, staged through LDS so each row leaves in 16-byte
+  // pieces that cover it contiguously
+  wait_vm_lds<0>();
+  barrier();
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int col = wn * 32 * NB + 32 * i + 8 * qq + 4 * half;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (g.bias && n0 + col < g.N) {  // N % 8 == 0: all four columns exist
+        const uint2 b4 = *reinterpret_cast<const uint2*>(g.bias + n0 + col);
+        bv[0] = bf16_lo(b4.x); bv[1] = bf16_hi(b4.x);
+        bv[2] = bf16_lo(b4.y); bv[3] = bf16_hi(b4.y);
+      }
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int row = wm * 32 * MB + 32 * j + l32;
+        const f32x16& a4 = acc[i][j];
+        uint2 o;
+        o.x = pack_bf16x2(a4[4 * qq] + bv[0], a4[4 * qq + 1] + bv[1]);
+        o.y = pack_bf16x2(a4[4 * qq + 2] + bv[2], a4[4 * qq + 3] + bv[3]);
+        *reinterpret_cast<uint2*>(lds + row * ES + col) = o;
+      }
+    }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
+#pragma unroll
+  for (int idx = tid; idx < BM * CPR; idx += 256) {
+    const int rrow = idx / CPR, c = idx % CPR;
+    const int m = m0 + rrow, n = n0 + c * 8;
+    if (m < g.M && n < g.N)
+      *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.N + n) =
+          *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s) {
+  if (g.K % 64 == 0 && int64_t(g.M) * g.K < (int64_t(1) << 31) &&
+      int64_t(g.N) * g.K < (int64_t(1) << 31)) {
+    // narrow outputs (the rank-r factor product) get 192 x 64 tiles, wide
+    // ones 256 x 128: at 4680 rows either grid is one round on 256 CUs
+    if (g.N <= 768) {
+      dim3 grid(((g.M + 191) / 192) * ((g.N + 63) / 64));
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4>), grid, dim3(256), 0, s, g);
+    } else {
+      dim3 grid(((g.M + 255) / 256) * ((g.N + 127) / 128));
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3>), grid, dim3(256), 0, s, g);
+    }
+    return hipGetLastError();
+  }
   const int nbn = (g.N + kBN - 1) / kBN;
   const int tiles128 = ((g.M + 127) / 128) * nbn;
   // enough workgroups to cover the 256 CUs twice, else halve the row tile
