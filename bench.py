@@ -31,10 +31,13 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
           "% MFMA/HBM peak")
 
-# HBM traffic of one attention launch from rocprofv3 --pmc (FETCH_SIZE and
-# WRITE_SIZE per dispatch, scaled by the counter-to-byte factor of a copy of
-# known size); None until measured for the current kernel.
-ATTN_TRAFFIC_BYTES = None
+# HBM traffic of one steady-state attention launch from rocprofv3 --pmc on
+# this workload: FETCH_SIZE 107,282 KiB and WRITE_SIZE 14,498 KiB per
+# dispatch (mean of the 7 chunk-5 dispatches), scaled by the counter-to-byte
+# factors of a 1 GiB device copy in the same run (read = 2 x FETCH_SIZE KiB,
+# written = WRITE_SIZE KiB).  Must be re-measured whenever the attention
+# kernel changes (None = not measured for the current kernel).
+ATTN_TRAFFIC_BYTES = (2 * 107282 + 14498) * 1024
 
 
 def parse():
