@@ -144,24 +144,17 @@ window_attn_kernel(AttnArgs a) {
   constexpr int KINST = kBN * D * 2 / 1024 / kWaves;  // K loads per wave per tile
   constexpr int VINST = D * kBN * 2 / 1024 / kWaves;  // V^T loads per wave per tile
   constexpr int NLD = KINST + VINST;                  // loads per wave per tile
-  // one array per stage, so that alias analysis can tell a stage being read
-  // from the stages the tile loads are writing (no needless waits)
-  __shared__ __attribute__((aligned(1024))) uint16_t lk0[kBN * D], lk1[kBN * D], lk2[kBN * D], lk3[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lv0[D * kBN], lv1[D * kBN], lv2[D * kBN], lv3[D * kBN];
-  static_assert(kStages == 4, "one LDS array per stage");
+  // one array per ring; the stage offsets (multiples of 16 KB for D = 128)
+  // are compile-time constants, so they fold into the LDS instructions'
+  // immediate offsets (under 64 KB) and each lane needs one address register
+  // per fragment position for all stages
+  __shared__ __attribute__((aligned(1024))) uint16_t lk[kStages * kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv[kStages * D * kBN];
   auto kstage = [&](auto tag) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int b = decltype(tag)::value;
-    if constexpr (b == 0) return lk0;
-    else if constexpr (b == 1) return lk1;
-    else if constexpr (b == 2) return lk2;
-    else return lk3;
+    return lk + decltype(tag)::value * (kBN * D);
   };
   auto vstage = [&](auto tag) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int b = decltype(tag)::value;
-    if constexpr (b == 0) return lv0;
-    else if constexpr (b == 1) return lv1;
-    else if constexpr (b == 2) return lv2;
-    else return lv3;
+    return lv + decltype(tag)::value * (D * kBN);
   };
   __shared__ uint32_t kbase[UST_MAX_WINDOW_FRAMES];
   __shared__ uint32_t vbase[UST_MAX_WINDOW_FRAMES];
