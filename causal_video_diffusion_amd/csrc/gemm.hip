@@ -159,8 +159,16 @@ gemm_nt_kernel(GemmArgs g) {
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
 }
+// sbase must be wave-uniform; it is passed through readfirstlane so that it
+// sits in scalar registers whatever the compiler proves about it
 __device__ __forceinline__ void load_lds16_s(const uint16_t* sbase, uint32_t voff_bytes, uint32_t m0) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(sbase), "{m0}"(m0));
+  // (readfirstlane returns int: widen through uint32_t, or a low word with
+  // bit 31 set would sign-extend into the high half)
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t su = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(p >> 32)))) << 32) |
+                      uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(p))));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(reinterpret_cast<const uint16_t*>(su)),
+               "{m0}"(m0));
 }
 // wait until at most N vector-memory ops of this wave are in flight and all
 // of its LDS reads have returned (so the next barrier orders them too)
