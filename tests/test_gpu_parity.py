@@ -201,6 +201,31 @@ def test_window_edge_cases():
             assert_close(_f64(o_gpu), o_ref, f"edge chunk {c}")
 
 
+@pytest.mark.parametrize("head_dim,pairs", [(64, (12, 10, 10)), (128, (22, 21, 21))])
+def test_window_attn_longest_window_short_frames(head_dim, pairs):
+    """The longest window the library accepts (128 frames: 2 sinks, 123
+    recent, 3 current) over 24-token frames, so every 64-key tile spans three
+    or four frames and every tile load takes the per-lane frame lookup; the
+    ring (130 slots) has wrapped.  Chunk 20 (the whole history, 63 frames)
+    and chunk 42 (exactly 128 frames) are compared row by row."""
+    w = wl.TINY.replace(name=f"longwin{head_dim}", wid=20 + head_dim // 64, n_heads=2,
+                        head_dim=head_dim, pairs=pairs, n_chunks=43, n_slots=130,
+                        n_sink=2, n_recent=123, n_tab_frames=129)
+    for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
+        if c not in (20, 42):
+            continue
+        frames, _ = B.ust_window_plan(g, ring.abi, 3 * c, w.n_recent)
+        assert len(frames) == (63 if c == 20 else 128)
+        print(f"[longest window D={head_dim} chunk {c}: {len(frames)} frames]", flush=True)
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c)
+        o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
+                                       w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+        assert_close(_f64(o_gpu), o_ref, f"longest window chunk {c} O")
+        assert_close(lse_gpu, lse_ref, f"longest window chunk {c} lse", max_abs=2e-2,
+                     rel_l2=1e-3)
+
+
 def test_nan_outside_window_and_determinism():
     """Poisoning every slot outside the window (and the value padding) with NaN
     leaves the output bit-identical; two runs agree bit for bit."""

@@ -113,6 +113,14 @@ def test_window_plan_errors(lib):
     big = B.Kv(None, None, 400, 0)
     with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
         B.ust_window_plan(g, big, 200, -1)
+    # exactly at the maximum (2 sinks + 123 recent + 3 current = 128 frames)
+    # is accepted, one frame more is not
+    ring130 = B.Kv(None, None, 130, 2)
+    frames, slots = B.ust_window_plan(g, ring130, 126, 123)
+    assert len(frames) == B.UST_MAX_WINDOW_FRAMES == 128
+    assert frames == [0, 1] + list(range(3, 129))
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, B.Kv(None, None, 131, 2), 127, 124)
 
 
 def _raw(lib, name, *args):
