@@ -9,11 +9,18 @@ frames = 18720 keys; 4680 queries; 12 heads x 128; rank-512 V/O):
 with every input resident in HBM when the timed region starts (the ring holds
 the window's earlier frames, written by the same path before timing).
 
+The attention schedule is the path's own choice by default (`--schedule
+auto`: the key-split ust_window_attn_split plus its merge kernel when the
+chunk has more (head, query tile) units than the GPU has compute units, else
+ust_window_attn with one workgroup per unit); `--schedule split|whole` forces
+one.
+
 Prints one JSON line.  `value` is the attention's algorithmic TFLOP per
-layer-chunk divided by the whole step's time; `roofline` is the attention
-kernel's own rate, timed with HIP events on its stream inside the timed
-region; `cpu_baseline` is the CPU fp64 oracle on a bounded sample of the same
-layer-chunk.
+layer-chunk divided by the whole step's time; `roofline` is the attention's
+own rate, timed with HIP events on its stream inside the timed region (for
+the split schedule the events span both the attention and the merge
+kernels); `cpu_baseline` is the CPU fp64 oracle on a bounded sample of the
+same layer-chunk.
 """
 from __future__ import annotations
 
@@ -31,21 +38,28 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
           "% MFMA/HBM peak")
 
-# HBM traffic of one steady-state attention launch from rocprofv3 --pmc on
-# this workload: FETCH_SIZE 107,282 KiB and WRITE_SIZE 14,498 KiB per
-# dispatch (mean of the 7 chunk-5 dispatches), scaled by the counter-to-byte
-# factors of a 1 GiB device copy in the same run (read = 2 x FETCH_SIZE KiB,
-# written = WRITE_SIZE KiB).  Must be re-measured whenever the attention
-# kernel changes (None = not measured for the current kernel).
-ATTN_TRAFFIC_BYTES = (2 * 107282 + 14498) * 1024
+# HBM traffic of one steady-state attention (rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE per dispatch on this workload, scaled by the counter-to-byte
+# factors of a 1 GiB device copy in the same run: read = 2 x FETCH_SIZE KiB,
+# written = WRITE_SIZE KiB), per (workload, schedule).  Must be re-measured
+# whenever the attention kernels change (absent = not measured for the
+# current kernels).
+ATTN_TRAFFIC_BYTES = {}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=("wan_window", "wan_720p"), default="wan_window",
+                    help="layer-chunk shape: the windowed Wan2.1-1.3B layer (default), or "
+                         "the same layer at 720p (45x80 tokens/frame, rank 256)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=("auto", "split", "whole"), default="auto",
+                    help="attention schedule: the path's choice (default), key-split "
+                         "over one workgroup per CU, or one workgroup per head and "
+                         "query tile")
     ap.add_argument("--cpu-reps", type=int, default=2,
                     help="layer-chunks the CPU oracle baseline runs")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -76,7 +90,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.load()
     torch.cuda.set_device(0)
-    w = wl.WAN_WINDOW
+    w = wl.ALL[args.workload]
     C = 5                                   # steady-state chunk
     F0 = 3 * C
     g = cvd.geom(*w.geom_tuple())
@@ -102,6 +116,19 @@ def main():
     frames, _ = B.ust_window_plan(g, ring.abi, F0, w.n_recent)
     n_k = len(frames) * w.T
     flops = attn_flops(w.n_q, n_k, w.head_dim, w.n_heads)
+    schedule = P.pick_attn_schedule(g) if args.schedule == "auto" else args.schedule
+    split = schedule == "split"
+    if split:
+        nbytes = B.ust_window_attn_work_bytes(g, 0)
+        work = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def attention():
+        if split:
+            B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
+                                    w.n_recent, 0.0, bufs.o, None, work, 0)
+        else:
+            B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
+                              w.n_recent, 0.0, bufs.o, None)
 
     # ev: None, or 5 events; all=False records only the two around the
     # attention kernel (each event costs ~2-3 µs of step time, so the timed
@@ -115,8 +142,7 @@ def main():
         B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
         if ev is not None:
             ev[2].record(stream)
-        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
-                          w.n_recent, 0.0, bufs.o, None)
+        attention()
         if ev is not None:
             ev[3].record(stream)
         P.lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
@@ -174,12 +200,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "wan_window layer-chunk: Wan2.1-1.3B self-attention layer, "
-                        "12 heads x 128, 30x52 = 1560 tokens/frame, 3-frame chunk = 4680 "
-                        "queries, window 3 sink + 6 recent + 3 current frames = 18720 keys, "
-                        "21-slot ring, rank-512 V/O, steady-state chunk 5",
+            "workload": f"{w.name} layer-chunk: Wan2.1-1.3B self-attention layer, "
+                        f"{w.n_heads} heads x {w.head_dim}, {w.grid_h}x{w.grid_w} = {w.T} "
+                        f"tokens/frame, 3-frame chunk = {w.n_q} queries, window {w.n_sink} "
+                        f"sink + {w.n_recent} recent + 3 current frames = {n_k} keys, "
+                        f"{w.n_slots}-slot ring, rank-{w.rank} V/O, steady-state chunk {C}",
             "n_q": w.n_q, "n_k": n_k, "n_heads": w.n_heads, "head_dim": w.head_dim,
             "rank": w.rank, "attn_gflop": round(flops / 1e9, 2),
+            "schedule": schedule,
         },
         "roofline": {
             "bound": "mfma",
@@ -187,8 +215,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": ATTN_TRAFFIC_BYTES,
-            "kernel": "window_attn_kernel<128>",
+            "traffic": ATTN_TRAFFIC_BYTES.get((w.name, schedule)),
+            "kernel": ("window_attn_kernel<128> + window_attn_combine_kernel<128>" if split
+                       else "window_attn_kernel<128>"),
             "kernel_us": round(attn_us, 2),
         },
         "stages_us": {k: round(v, 2) for k, v in stage.items()},
@@ -249,7 +278,7 @@ def cpu_baseline(w, C, reps):
         "cores": int(cores),
         "kind": "oracle",
         "ms_per_step": round(dt * 1e3, 1),
-        "sample": f"the same wan_window steady-state layer-chunk, whole, {reps} times: fp64 "
+        "sample": f"the same {w.name} steady-state layer-chunk, whole, {reps} times: fp64 "
                   f"V projection, KV append, attention of all {w.n_q} queries over "
                   f"{len(frames) * w.T} keys (materialised softmax in 1024-row blocks) and O "
                   f"projection; value = attention flops / mean layer-chunk wall time; "

@@ -20,8 +20,9 @@ STATUS = {0: "UST_OK", 1: "UST_E_NULL", 2: "UST_E_SHAPE", 3: "UST_E_RANGE",
 
 # every entry point the header declares
 EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
-           "ust_window_attn", "ust_lowrank_proj", "ust_slot_of_frame",
-           "ust_window_plan", "ust_status_str", "ust_last_error")
+           "ust_window_attn", "ust_window_attn_work_bytes", "ust_window_attn_split",
+           "ust_lowrank_proj", "ust_slot_of_frame", "ust_window_plan",
+           "ust_status_str", "ust_last_error")
 
 
 class UstError(RuntimeError):
@@ -56,6 +57,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                           "`python -m causal_video_diffusion_amd.build`")
     lib = ctypes.CDLL(path)
     P, I32, F32, F64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double
+    SZ = ctypes.c_size_t
     GP, KP = ctypes.POINTER(Geom), ctypes.POINTER(Kv)
     IP = ctypes.POINTER(ctypes.c_int32)
     sig = {
@@ -63,6 +65,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "ust_rope_table_build": (I32, [GP, I32, F64, P, P, P]),
         "ust_kv_append": (I32, [GP, KP, P, P, P, P, I32, I32, P]),
         "ust_window_attn": (I32, [GP, KP, P, P, P, I32, I32, I32, F32, P, P, P]),
+        "ust_window_attn_work_bytes": (SZ, [GP, I32]),
+        "ust_window_attn_split": (I32, [GP, KP, P, P, P, I32, I32, I32, F32, P, P, P, SZ,
+                                        I32, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_slot_of_frame": (I32, [KP, I32]),
         "ust_window_plan": (I32, [GP, KP, I32, I32, IP, IP, I32, IP]),
@@ -137,6 +142,23 @@ def ust_window_attn(g: Geom, ring: Kv, q, cos_tab, sin_tab, n_tab_frames: int,
                                   _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
                                   frame_start, n_recent, scale, _ptr(out),
                                   _ptr(lse), _stream(stream)))
+
+
+def ust_window_attn_work_bytes(g: Geom, n_workgroups: int = 0) -> int:
+    return load().ust_window_attn_work_bytes(ctypes.byref(g), n_workgroups)
+
+
+def ust_window_attn_split(g: Geom, ring: Kv, q, cos_tab, sin_tab, n_tab_frames: int,
+                          frame_start: int, n_recent: int, scale: float, out,
+                          lse=None, work=None, n_workgroups: int = 0,
+                          stream=None) -> None:
+    """work: a device tensor of at least ust_window_attn_work_bytes bytes."""
+    nbytes = 0 if work is None else work.numel() * work.element_size()
+    _check(load().ust_window_attn_split(ctypes.byref(g), ctypes.byref(ring), _ptr(q),
+                                        _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
+                                        frame_start, n_recent, scale, _ptr(out),
+                                        _ptr(lse), _ptr(work), nbytes, n_workgroups,
+                                        _stream(stream)))
 
 
 def ust_lowrank_proj(x, a, b, bias, t_work, y, M: int, K: int, r: int, N: int,

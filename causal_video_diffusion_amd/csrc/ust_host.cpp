@@ -240,10 +240,26 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
   }
 }
 
-ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
-                           const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
-                           int32_t frame_start, int32_t n_recent, float scale, void* out,
-                           float* lse_opt, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Compute units of the current device, or -1.
+int32_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n > 0 ? n : -1;
+}
+
+constexpr int32_t kMaxAttnWorkgroups = 1 << 16;
+
+// ust_window_attn (work == nullptr) and ust_window_attn_split
+ust_status window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
+                       const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
+                       int32_t frame_start, int32_t n_recent, float scale, void* out,
+                       float* lse_opt, bool split, void* work, size_t work_bytes,
+                       int32_t n_workgroups, hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
@@ -286,10 +302,56 @@ ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
     a.frame_start = frame_start;
     a.n_frames = n;
     a.qscale = sc * 1.4426950408889634f;  // log2(e): softmax runs in base 2
+    if (split) {
+      if (n_workgroups > kMaxAttnWorkgroups)
+        return fail(UST_E_SHAPE, "n_workgroups %d exceeds %d", n_workgroups, kMaxAttnWorkgroups);
+      const int32_t nwg = n_workgroups > 0 ? n_workgroups : device_cus();
+      if (nwg <= 0) return fail(UST_E_HIP, "cannot query the device's compute units");
+      const size_t need = ust::window_attn_work_bytes(g->head_dim, nwg);
+      if (!work) return fail(UST_E_NULL, "work is NULL");
+      if (!aligned16(work)) return fail(UST_E_ALIGN, "work must be 16-byte aligned");
+      if (work_bytes < need)
+        return fail(UST_E_SHAPE, "work holds %zu bytes, %zu needed for %d workgroups",
+                    work_bytes, need, nwg);
+      a.work_o = static_cast<float*>(work);
+      a.n_wg = nwg;
+    }
     return hip_status(ust::launch_window_attn(a, stream), "window_attn launch");
   } catch (...) {
     return fail(UST_E_HIP, "internal error");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
+                           const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
+                           int32_t frame_start, int32_t n_recent, float scale, void* out,
+                           float* lse_opt, hipStream_t stream) {
+  return window_attn(g, kv, q, cos_tab, sin_tab, n_tab_frames, frame_start, n_recent, scale,
+                     out, lse_opt, false, nullptr, 0, 0, stream);
+}
+
+size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups) {
+  try {
+    if (check_geom(g) != UST_OK || n_workgroups > kMaxAttnWorkgroups) return 0;
+    const int32_t nwg = n_workgroups > 0 ? n_workgroups : device_cus();
+    if (nwg <= 0) return 0;
+    return ust::window_attn_work_bytes(g->head_dim, nwg);
+  } catch (...) {
+    return 0;
+  }
+}
+
+ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void* q,
+                                 const float* cos_tab, const float* sin_tab,
+                                 int32_t n_tab_frames, int32_t frame_start, int32_t n_recent,
+                                 float scale, void* out, float* lse_opt, void* work,
+                                 size_t work_bytes, int32_t n_workgroups, hipStream_t stream) {
+  return window_attn(g, kv, q, cos_tab, sin_tab, n_tab_frames, frame_start, n_recent, scale,
+                     out, lse_opt, true, work, work_bytes, n_workgroups, stream);
 }
 
 ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const void* bias,

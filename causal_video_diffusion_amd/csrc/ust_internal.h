@@ -42,6 +42,14 @@ struct AttnArgs {
   int32_t frame_start;       // absolute frame of query token 0
   int32_t n_frames;          // frames in the window
   float qscale;              // scale * log2(e), folded into the rotated query
+  // Key-split schedule.  work_o == nullptr: one workgroup per (head, query
+  // tile).  Otherwise the (head, query tile, key tile) sequence is divided
+  // evenly over n_wg workgroups; a (head, query tile) split between
+  // workgroups leaves normalised partial outputs and their log-sum-exps here
+  // for the combine kernel.
+  float* work_o;             // [2 n_wg][256][D] fp32
+  float* work_l;             // [2 n_wg][256] fp32 (natural log), set by the launcher
+  int32_t n_wg;              // workgroups to divide the work over (>= 1)
   int32_t slots[UST_MAX_WINDOW_FRAMES];
 };
 
@@ -56,6 +64,8 @@ struct GemmArgs {
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
+// workspace bytes of the key-split schedule over n_wg workgroups
+size_t window_attn_work_bytes(int32_t head_dim, int32_t n_wg);
 hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
 
 }  // namespace ust

@@ -42,9 +42,16 @@
 //  * Workgroups are numbered so that each XCD (8 per chip, dispatched round
 //    robin) gets a contiguous run of (head, query tile) work: the workgroups
 //    streaming one head's K/V share an L2.
+//  * Two schedules (attn_schedule.h).  Either each workgroup owns one (head,
+//    query tile) over all key tiles, or the (head, query tile, key tile)
+//    sequence is cut into equal ranges, one per workgroup (one per CU), so a
+//    chunk with fewer query tiles than CUs still fills the chip.  A query
+//    tile split between workgroups leaves each part's normalised output and
+//    log-sum-exp in a workspace, and a second kernel merges them.
 
 #include <type_traits>
 
+#include "attn_schedule.h"
 #include "ust_device.h"
 #include "ust_internal.h"
 
@@ -168,9 +175,6 @@ window_attn_kernel(AttnArgs a) {
   __shared__ uint32_t vbase[UST_MAX_WINDOW_FRAMES];
 
   const int nqt = (a.NQ + kBM - 1) / kBM;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = w / nqt;
-  const int q0 = (w % nqt) * kBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,42 +186,12 @@ window_attn_kernel(AttnArgs a) {
   const int nk = a.n_frames * T;
   const int ntiles = (nk + kBN - 1) / kBN;
 
-  for (int i = tid; i < a.n_frames; i += 512) {
-    kbase[i] = uint32_t((a.slots[i] * a.H + h) * T * D);
-    vbase[i] = uint32_t((a.slots[i] * a.H + h) * D * TV);
-  }
-
-  // ---- query fragments: RoPE at the query's own position, scale, bf16 ----
-  const int qn = q0 + wave * 32 + l32;
-  const bool qvalid = qn < a.NQ;
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = a.q + (int64_t(qn) * a.H + h) * D;
-    const int64_t trow = (int64_t(a.frame_start) * T + qn) * (D / 2);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int d0 = 16 * s + 8 * half;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      float4 cs = make_float4(0, 0, 0, 0), sn = make_float4(0, 0, 0, 0);
-      if (qvalid) {
-        raw = *reinterpret_cast<const uint4*>(qp + d0);
-        cs = *reinterpret_cast<const float4*>(a.cos_tab + trow + d0 / 2);
-        sn = *reinterpret_cast<const float4*>(a.sin_tab + trow + d0 / 2);
-      }
-      const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
-      const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
-      const float s4[4] = {sn.x, sn.y, sn.z, sn.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_lo(in[e]), x1 = bf16_hi(in[e]);
-        o[e] = pack_bf16x2((x0 * c4[e] - x1 * s4[e]) * a.qscale,
-                           (x0 * s4[e] + x1 * c4[e]) * a.qscale);
-      }
-      qf[s] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  }
-  __syncthreads();  // kbase / vbase visible
+  // ---- this workgroup's share of the work (attn_schedule.h) ----
+  const int G = gridDim.x;
+  const int64_t work_total = int64_t(nqt) * a.H * ntiles;
+  const int w = xcd_remap(blockIdx.x, G);
+  const int64_t x_begin = wg_range_start(w, work_total, G);
+  const int64_t x_end = wg_range_start(w + 1, work_total, G);
 
   // ---- per-lane constants of the tile loads ----
   // K load i of wave w fills LDS bytes [(w*KINST + i) KB, +1 KB): key row
@@ -247,242 +221,402 @@ window_attn_kernel(AttnArgs a) {
     for (int q = 0; q < 4; ++q) voffr[q] = l32 * kBN + (((2 * q + half) ^ vswz(l32)) * 8);
   }
 
-  // Issue the global->LDS loads of tile t (starting at frame lfi, token lt0).
-  // kfb / vfb: the frame's key and value slot bases (wave-uniform), reloaded
-  // only when the load position moves to the next frame.
-  int lfi = 0, lt0 = 0;   // position of the next tile to load
-  const uint16_t* kfb = a.k_cache + (int64_t(a.slots[0]) * a.H + h) * T * D;
-  const uint16_t* vfb = a.v_cache + (int64_t(a.slots[0]) * a.H + h) * D * TV;
-  auto next_frame = [&]() __attribute__((always_inline)) {
-    ++lfi;
-    if (lfi < a.n_frames) {
-      kfb = a.k_cache + (int64_t(a.slots[lfi]) * a.H + h) * T * D;
-      vfb = a.v_cache + (int64_t(a.slots[lfi]) * a.H + h) * D * TV;
+  // One segment per unit the range meets: a whole unit, or key tiles
+  // k0 .. k0+nseg-1 of one.
+  for (int64_t x = x_begin; x < x_end;) {
+    const AttnSegment sg = attn_segment(x, x_begin, x_end, w, ntiles, work_total, G);
+    const int k0 = sg.k0;
+    const int nseg = sg.n;
+    const int slot = sg.slot;
+    const int h = sg.unit / nqt;
+    const int q0 = (sg.unit % nqt) * kBM;
+    x = sg.next;
+
+    __syncthreads();  // the previous segment is done with kbase / vbase
+    for (int i = tid; i < a.n_frames; i += 512) {
+      kbase[i] = uint32_t((a.slots[i] * a.H + h) * T * D);
+      vbase[i] = uint32_t((a.slots[i] * a.H + h) * D * TV);
     }
-  };
-  auto issue = [&](int t, auto buf_tag) __attribute__((always_inline)) {
-    const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr(kstage(buf_tag) + wave * KINST * 512));
-    const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(vstage(buf_tag) + wave * VINST * 512));
-    if (lt0 + kBN <= T && t * kBN + kBN <= nk) {
-      // whole tile inside one frame: uniform base + lane constants
-      const uint16_t* kb = kfb + lt0 * D;
-      const uint16_t* vb = vfb + lt0;
-#pragma unroll
-      for (int i = 0; i < KINST; ++i) load_lds16_s(kb, uint32_t(koff[i]) * 2u, lk + i * 1024);
-#pragma unroll
-      for (int i = 0; i < VINST; ++i) load_lds16_s(vb, uint32_t(voff[i]) * 2u, lv + i * 1024);
-    } else {
-      // straddles frames or runs past the window: per-lane frame lookup;
-      // keys past the window are pointed at the window's first key (finite
-      // data whose probability is masked to zero)
-#pragma unroll
-      for (int i = 0; i < KINST; ++i) {
-        const int row = KRPI * (wave * KINST + i) + lane / KCPR;
-        int tt = lt0 + row, f = lfi;
-        while (tt >= T) { tt -= T; ++f; }
-        if (f >= a.n_frames) { f = 0; tt = 0; }
-        load_lds16(a.k_cache + kbase[f] + uint32_t(tt * D) + (koff[i] - row * D), lk + i * 1024);
-      }
-#pragma unroll
-      for (int i = 0; i < VINST; ++i) {
-        const int d = 8 * (wave * VINST + i) + lane / 8;
-        const int kc = (lane % 8) ^ vswz(d);
-        int tt = lt0 + 8 * kc, f = lfi;
-        while (tt >= T) { tt -= T; ++f; }
-        if (f >= a.n_frames) { f = 0; tt = 0; }
-        load_lds16(a.v_cache + vbase[f] + uint32_t(tt) + uint32_t(d * TV), lv + i * 1024);
-      }
-    }
-    lt0 += kBN;
-    while (lt0 >= T) {
-      lt0 -= T;
-      next_frame();
-    }
-  };
 
-  f32x16 oacc[DB];
+    // ---- query fragments: RoPE at the query's own position, scale, bf16 ----
+    const int qn = q0 + wave * 32 + l32;
+    const bool qvalid = qn < a.NQ;
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qp = a.q + (int64_t(qn) * a.H + h) * D;
+      const int64_t trow = (int64_t(a.frame_start) * T + qn) * (D / 2);
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-  float mref = 0.f;   // reference max (log2 units) of this lane's query
-  float lrow = 0.f;   // this lane's share of the running sum, relative to mref
-  f32x16 sacc[2];     // S^T - mref of the tile being computed
-  bf16x8 pf[2][2];    // bf16 probabilities of the tile awaiting PV
-
-  // ---- S^T - mref = K Q^T + (-mref), two 32-key blocks ----
-  // The fragment reads run kPre ahead of the MFMAs that consume them (the
-  // scheduling-group barriers pin that order), so the MFMA pipe does not
-  // wait on LDS latency.
-  auto qk = [&](auto buf_tag) __attribute__((always_inline)) {
-    const uint16_t* K = kstage(buf_tag);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = -mref;
-    bf16x8 kf[2 * KS];
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i)
-      kf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[i >> 1] + (i & 1) * 32 * D));
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
-    sched_pipeline<2 * KS>();
-  };
-
-  // ---- O^T += V^T P^T ----
-  auto pv = [&](auto buf_tag) __attribute__((always_inline)) {
-    const uint16_t* V = vstage(buf_tag);
-    // fragment i: key chunk 4 kb + 2 g + half of dim 32 b + l32, with
-    // q = 2 kb + g = i / DB, b = i % DB
-    bf16x8 vf[4 * DB];
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i)
-      vf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(V + voffr[i / DB] + (i % DB) * 32 * kBN));
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i)
-      oacc[i % DB] = mfma32(vf[i], pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
-    sched_pipeline<4 * DB>();
-  };
-
-  // ---- online softmax of tile t: bf16 probabilities into pf ----
-  auto softmax = [&](int t) __attribute__((always_inline)) {
-    if (t == ntiles - 1 && ntiles * kBN > nk) {
-      asm volatile("; last tile: keys past the window end");
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * kBN + 32 * kb + 16 * (r / 8) + 8 * half + (r % 8);
-          if (key >= nk) sacc[kb][r] = -INFINITY;
+      for (int s = 0; s < KS; ++s) {
+        const int d0 = 16 * s + 8 * half;
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        float4 cs = make_float4(0, 0, 0, 0), sn = make_float4(0, 0, 0, 0);
+        if (qvalid) {
+          raw = *reinterpret_cast<const uint4*>(qp + d0);
+          cs = *reinterpret_cast<const float4*>(a.cos_tab + trow + d0 / 2);
+          sn = *reinterpret_cast<const float4*>(a.sin_tab + trow + d0 / 2);
         }
-    }
-    // tile max: a tree of independent max3 ops, not one long dependent chain
-    float m4[4];
+        const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
+        const float s4[4] = {sn.x, sn.y, sn.z, sn.w};
+        uint32_t o[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int kb = c >> 1, r0 = 8 * (c & 1);
-      m4[c] = fmaxf(fmaxf(fmaxf(sacc[kb][r0], sacc[kb][r0 + 1]), sacc[kb][r0 + 2]),
-                    fmaxf(fmaxf(sacc[kb][r0 + 3], sacc[kb][r0 + 4]),
-                          fmaxf(fmaxf(sacc[kb][r0 + 5], sacc[kb][r0 + 6]), sacc[kb][r0 + 7])));
-    }
-    float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    tmax = pair_max(tmax);
-    const bool need = (t == 0) || (tmax > kRescale);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float shift = need ? tmax : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-shift);
-      mref += shift;
-      lrow *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
-    }
-    // probabilities in place (32 independent exp2), the row sum in fp32 in
-    // four independent partial sums (plain adds: dot-product instructions
-    // would contend with the partner wave's MFMAs), then bf16 pairs
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ls[r & 3] += sacc[kb][r];
-    lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pk[e] = pack_bf16x2(sacc[kb][8 * g + 2 * e], sacc[kb][8 * g + 2 * e + 1]);
-        pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = bf16_lo(in[e]), x1 = bf16_hi(in[e]);
+          o[e] = pack_bf16x2((x0 * c4[e] - x1 * s4[e]) * a.qscale,
+                             (x0 * s4[e] + x1 * c4[e]) * a.qscale);
+        }
+        qf[s] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
       }
-  };
-
-  // ---- the phase schedule ----
-  // Every wave runs the same sequence; group B starts one barrier later, so
-  // its phases are offset by one from group A's:
-  //   MFMA phase t:    QK(t); PV(t-1); barrier
-  //   softmax phase t: request own share of tile t+L; softmax(t); wait for own
-  //                    share of tile t+L-1; barrier
-  // with L = 2 for group A and L = 3 for group B, so every share of tile u is
-  // in LDS before group A's MFMA phase u, and the loads and their waits sit in
-  // softmax phases, under the partner wave's MFMA phase.  Tile u lives in LDS
-  // stage u % 4 from its first request (group B's softmax phase u-3) until
-  // group B's PV(u) (its MFMA phase u+1).
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  const int lead = group_a ? 2 : 3;
-  auto step = [&](int t, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);
-    if (t < ntiles) qk(cur);     // first, so its scores are ready for softmax(t)
-    if (t >= 1) pv(prev);
-    __builtin_amdgcn_s_setprio(0);
-    barrier();
-    const int u = t + lead;      // tile this wave requests now
-    if (u < ntiles) {
-      if (group_a) issue(u, st2);
-      else issue(u, st3);
     }
-    if (t < ntiles) softmax(t);
-    if (u < ntiles) wait_vmcnt<NLD>();   // own share of tile u-1 landed
-    else wait_vmcnt<0>();
-    barrier();
-  };
+    __syncthreads();  // kbase / vbase visible
 
-  issue(0, S0{});
-  if (ntiles > 1) issue(1, S1{});
-  if (!group_a && ntiles > 2) issue(2, S2{});
-  wait_vmcnt<0>();
-  barrier();                        // tiles 0 .. lead-1 are in LDS
-  if (!group_a) barrier();          // group B runs one phase behind
-  for (int t = 0; t <= ntiles; t += 4) {
-    step(t, S0{}, S3{}, S2{}, S3{});
-    if (t + 1 <= ntiles) step(t + 1, S1{}, S0{}, S3{}, S0{});
-    if (t + 2 <= ntiles) step(t + 2, S2{}, S1{}, S0{}, S1{});
-    if (t + 3 <= ntiles) step(t + 3, S3{}, S2{}, S1{}, S2{});
-  }
-  if (group_a) barrier();           // match group B's extra barrier
+    // Issue the global->LDS loads of key tile t (starting at frame lfi, token
+    // lt0).  kfb / vfb: the frame's key and value slot bases (wave-uniform),
+    // reloaded only when the load position moves to the next frame.
+    int lfi = k0 * kBN / T;   // position of the next tile to load
+    int lt0 = k0 * kBN - lfi * T;
+    const uint16_t* kfb = a.k_cache + (int64_t(a.slots[lfi]) * a.H + h) * T * D;
+    const uint16_t* vfb = a.v_cache + (int64_t(a.slots[lfi]) * a.H + h) * D * TV;
+    auto next_frame = [&]() __attribute__((always_inline)) {
+      ++lfi;
+      if (lfi < a.n_frames) {
+        kfb = a.k_cache + (int64_t(a.slots[lfi]) * a.H + h) * T * D;
+        vfb = a.v_cache + (int64_t(a.slots[lfi]) * a.H + h) * D * TV;
+      }
+    };
+    auto issue = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+      const uint32_t lk = __builtin_amdgcn_readfirstlane(lds_addr(kstage(buf_tag) + wave * KINST * 512));
+      const uint32_t lv = __builtin_amdgcn_readfirstlane(lds_addr(vstage(buf_tag) + wave * VINST * 512));
+      if (lt0 + kBN <= T && t * kBN + kBN <= nk) {
+        // whole tile inside one frame: uniform base + lane constants
+        const uint16_t* kb = kfb + lt0 * D;
+        const uint16_t* vb = vfb + lt0;
+#pragma unroll
+        for (int i = 0; i < KINST; ++i) load_lds16_s(kb, uint32_t(koff[i]) * 2u, lk + i * 1024);
+#pragma unroll
+        for (int i = 0; i < VINST; ++i) load_lds16_s(vb, uint32_t(voff[i]) * 2u, lv + i * 1024);
+      } else {
+        // straddles frames or runs past the window: per-lane frame lookup;
+        // keys past the window are pointed at the window's first key (finite
+        // data whose probability is masked to zero)
+#pragma unroll
+        for (int i = 0; i < KINST; ++i) {
+          const int row = KRPI * (wave * KINST + i) + lane / KCPR;
+          int tt = lt0 + row, f = lfi;
+          while (tt >= T) { tt -= T; ++f; }
+          if (f >= a.n_frames) { f = 0; tt = 0; }
+          load_lds16(a.k_cache + kbase[f] + uint32_t(tt * D) + (koff[i] - row * D), lk + i * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < VINST; ++i) {
+          const int d = 8 * (wave * VINST + i) + lane / 8;
+          const int kc = (lane % 8) ^ vswz(d);
+          int tt = lt0 + 8 * kc, f = lfi;
+          while (tt >= T) { tt -= T; ++f; }
+          if (f >= a.n_frames) { f = 0; tt = 0; }
+          load_lds16(a.v_cache + vbase[f] + uint32_t(tt) + uint32_t(d * TV), lv + i * 1024);
+        }
+      }
+      lt0 += kBN;
+      while (lt0 >= T) {
+        lt0 -= T;
+        next_frame();
+      }
+    };
 
-  // ---- epilogue: normalise, store bf16 O and the log-sum-exp ----
-  const float ltot = pair_sum(lrow);
-  const float inv = 1.f / ltot;
-  if (qvalid) {
-    uint16_t* op = a.out + (int64_t(qn) * a.H + h) * D;
+    f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * b + 8 * g + 4 * half;
-        uint2 v;
-        v.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-        v.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d) = v;
+      for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+    float mref = 0.f;   // reference max (log2 units) of this lane's query
+    float lrow = 0.f;   // this lane's share of the running sum, relative to mref
+    f32x16 sacc[2];     // S^T - mref of the tile being computed
+    bf16x8 pf[2][2];    // bf16 probabilities of the tile awaiting PV
+
+    // ---- S^T - mref = K Q^T + (-mref), two 32-key blocks ----
+    // The fragment reads run kPre ahead of the MFMAs that consume them (the
+    // scheduling-group barriers pin that order), so the MFMA pipe does not
+    // wait on LDS latency.
+    auto qk = [&](auto buf_tag) __attribute__((always_inline)) {
+      const uint16_t* K = kstage(buf_tag);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = -mref;
+      bf16x8 kf[2 * KS];
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i)
+        kf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[i >> 1] + (i & 1) * 32 * D));
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
+      sched_pipeline<2 * KS>();
+    };
+
+    // ---- O^T += V^T P^T ----
+    auto pv = [&](auto buf_tag) __attribute__((always_inline)) {
+      const uint16_t* V = vstage(buf_tag);
+      // fragment i: key chunk 4 kb + 2 g + half of dim 32 b + l32, with
+      // q = 2 kb + g = i / DB, b = i % DB
+      bf16x8 vf[4 * DB];
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i)
+        vf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(V + voffr[i / DB] + (i % DB) * 32 * kBN));
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i)
+        oacc[i % DB] = mfma32(vf[i], pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
+      sched_pipeline<4 * DB>();
+    };
+
+    // ---- online softmax of the segment's j-th tile (key tile t = k0 + j):
+    // bf16 probabilities into pf ----
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+      const int t = k0 + j;
+      if (t == ntiles - 1 && ntiles * kBN > nk) {
+        asm volatile("; last tile: keys past the window end");
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t * kBN + 32 * kb + 16 * (r / 8) + 8 * half + (r % 8);
+            if (key >= nk) sacc[kb][r] = -INFINITY;
+          }
       }
-    if (a.lse && half == 0)
-      a.lse[int64_t(h) * a.NQ + qn] = (mref + __builtin_log2f(ltot)) * 0.6931471805599453f;
+      // tile max: a tree of independent max3 ops, not one long dependent chain
+      float m4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kb = c >> 1, r0 = 8 * (c & 1);
+        m4[c] = fmaxf(fmaxf(fmaxf(sacc[kb][r0], sacc[kb][r0 + 1]), sacc[kb][r0 + 2]),
+                      fmaxf(fmaxf(sacc[kb][r0 + 3], sacc[kb][r0 + 4]),
+                            fmaxf(fmaxf(sacc[kb][r0 + 5], sacc[kb][r0 + 6]), sacc[kb][r0 + 7])));
+      }
+      float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      tmax = pair_max(tmax);
+      const bool need = (j == 0) || (tmax > kRescale);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float shift = need ? tmax : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        mref += shift;
+        lrow *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
+      }
+      // probabilities in place (32 independent exp2), the row sum in fp32 in
+      // four independent partial sums (plain adds: dot-product instructions
+      // would contend with the partner wave's MFMAs), then bf16 pairs
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls[r & 3] += sacc[kb][r];
+      lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pk[e] = pack_bf16x2(sacc[kb][8 * g + 2 * e], sacc[kb][8 * g + 2 * e + 1]);
+          pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+    };
+
+    // ---- the phase schedule ----
+    // Tiles are counted from the segment's first (j = 0 is key tile k0).
+    // Every wave runs the same sequence; group B starts one barrier later, so
+    // its phases are offset by one from group A's:
+    //   MFMA phase j:    QK(j); PV(j-1); barrier
+    //   softmax phase j: request own share of tile j+L; softmax(j); wait for own
+    //                    share of tile j+L-1; barrier
+    // with L = 2 for group A and L = 3 for group B, so every share of tile v is
+    // in LDS before group A's MFMA phase v, and the loads and their waits sit in
+    // softmax phases, under the partner wave's MFMA phase.  Tile v lives in LDS
+    // stage v % 4 from its first request (group B's softmax phase v-3) until
+    // group B's PV(v) (its MFMA phase v+1).
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    const int lead = group_a ? 2 : 3;
+    auto step = [&](int j, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(2);
+      if (j < nseg) qk(cur);       // first, so its scores are ready for softmax(j)
+      if (j >= 1) pv(prev);
+      __builtin_amdgcn_s_setprio(0);
+      barrier();
+      const int v = j + lead;      // tile this wave requests now
+      if (v < nseg) {
+        if (group_a) issue(k0 + v, st2);
+        else issue(k0 + v, st3);
+      }
+      if (j < nseg) softmax(j);
+      if (v < nseg) wait_vmcnt<NLD>();   // own share of tile v-1 landed
+      else wait_vmcnt<0>();
+      barrier();
+    };
+
+    issue(k0, S0{});
+    if (nseg > 1) issue(k0 + 1, S1{});
+    if (!group_a && nseg > 2) issue(k0 + 2, S2{});
+    wait_vmcnt<0>();
+    barrier();                        // tiles 0 .. lead-1 are in LDS
+    if (!group_a) barrier();          // group B runs one phase behind
+    for (int j = 0; j <= nseg; j += 4) {
+      step(j, S0{}, S3{}, S2{}, S3{});
+      if (j + 1 <= nseg) step(j + 1, S1{}, S0{}, S3{}, S0{});
+      if (j + 2 <= nseg) step(j + 2, S2{}, S1{}, S0{}, S1{});
+      if (j + 3 <= nseg) step(j + 3, S3{}, S2{}, S1{}, S2{});
+    }
+    if (group_a) barrier();           // match group B's extra barrier
+
+    // ---- epilogue: normalise, store bf16 O and the log-sum-exp, or the
+    // partial result of a split unit ----
+    const float ltot = pair_sum(lrow);
+    const float inv = 1.f / ltot;
+    const float lse_nat = (mref + __builtin_log2f(ltot)) * 0.6931471805599453f;
+    if (slot >= 0) {
+      if (qvalid) {
+        const int row = wave * 32 + l32;
+        float* po = a.work_o + (int64_t(slot) * kBM + row) * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = 32 * b + 8 * g + 4 * half;
+            *reinterpret_cast<float4*>(po + d) =
+                make_float4(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv,
+                            oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+          }
+        if (half == 0) a.work_l[int64_t(slot) * kBM + row] = lse_nat;
+      }
+    } else if (qvalid) {
+      uint16_t* op = a.out + (int64_t(qn) * a.H + h) * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * b + 8 * g + 4 * half;
+          uint2 v;
+          v.x = pack_bf16x2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
+          v.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d) = v;
+        }
+      if (a.lse && half == 0) a.lse[int64_t(h) * a.NQ + qn] = lse_nat;
+    }
+  }  // segments
+}
+
+// Merge the partial results of units that the key-split schedule divided
+// between workgroups.  With per-part normalised outputs O_i and log-sum-exps
+// L_i: O = sum_i e^(L_i - M) O_i / sum_i e^(L_i - M), L = M + ln sum_i
+// e^(L_i - M), M = max_i L_i, taken part by part with a running maximum.
+// One block per 64 query rows of a unit; each thread owns 4 dims of
+// kMergeRows / (256 / (D/4)) rows and keeps all of them in flight.
+constexpr int kMergeRows = 64;
+template <int D>
+__global__ void __launch_bounds__(256) window_attn_combine_kernel(AttnArgs a) {
+  constexpr int CPR = D / 4;                  // float4 chunks per row
+  constexpr int RSTEP = 256 / CPR;            // rows apart of one thread's rows
+  constexpr int PER = kMergeRows / RSTEP;     // rows per thread
+  constexpr int BPU = kBM / kMergeRows;       // blocks per unit
+  const int nqt = (a.NQ + kBM - 1) / kBM;
+  const int ntiles = (a.n_frames * a.T + kBN - 1) / kBN;
+  const int G = a.n_wg;
+  const int64_t total = int64_t(nqt) * a.H * ntiles;
+  const int u = blockIdx.x / BPU;
+  if (attn_unit_whole(u, ntiles, total, G)) return;   // written by its workgroup
+  const int64_t ue = int64_t(u + 1) * ntiles;
+  const int h = u / nqt;
+  const int c = threadIdx.x % CPR;
+  const int row0 = (blockIdx.x % BPU) * kMergeRows + threadIdx.x / CPR;
+  float m[PER], sum[PER];
+  float4 acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    m[k] = -INFINITY;
+    sum[k] = 0.f;
+    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int b = attn_unit_first_wg(u, ntiles, total, G); b < G && wg_range_start(b, total, G) < ue;
+       ++b) {
+    const int slot = attn_partial_slot(b, u, ntiles, total, G);
+    const float* lp = a.work_l + int64_t(slot) * kBM;
+    const float* op = a.work_o + int64_t(slot) * kBM * D + 4 * c;
+    float l[PER];
+    float4 o[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int row = row0 + k * RSTEP;
+      l[k] = lp[row];
+      o[k] = *reinterpret_cast<const float4*>(op + int64_t(row) * D);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const float mn = fmaxf(m[k], l[k]);
+      const float sa = expf(m[k] - mn);   // 0 on the first part (m = -inf)
+      const float e = expf(l[k] - mn);
+      m[k] = mn;
+      sum[k] = sum[k] * sa + e;
+      acc[k].x = acc[k].x * sa + e * o[k].x;
+      acc[k].y = acc[k].y * sa + e * o[k].y;
+      acc[k].z = acc[k].z * sa + e * o[k].z;
+      acc[k].w = acc[k].w * sa + e * o[k].w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int qn = (u % nqt) * kBM + row0 + k * RSTEP;
+    if (qn >= a.NQ) continue;   // rows past the chunk: no partial was written
+    const float inv = 1.f / sum[k];
+    uint2 v;
+    v.x = pack_bf16x2(acc[k].x * inv, acc[k].y * inv);
+    v.y = pack_bf16x2(acc[k].z * inv, acc[k].w * inv);
+    *reinterpret_cast<uint2*>(a.out + (int64_t(qn) * a.H + h) * D + 4 * c) = v;
+    if (a.lse && c == 0) a.lse[int64_t(h) * a.NQ + qn] = m[k] + logf(sum[k]);
   }
 }
 
 }  // namespace
 
-hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s) {
+size_t window_attn_work_bytes(int32_t head_dim, int32_t n_wg) {
+  return size_t(2) * size_t(n_wg) * kBM * (size_t(head_dim) + 1) * sizeof(float);
+}
+
+hipError_t launch_window_attn(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
   const int nqt = (a.NQ + kBM - 1) / kBM;
-  dim3 grid(nqt * a.H);
+  const int units = nqt * a.H;
+  const int ntiles = (a.n_frames * a.T + kBN - 1) / kBN;
+  const int64_t total = int64_t(units) * ntiles;
+  // one workgroup per unit, or the requested count (at most one per step);
+  // the workspace is laid out for the requested count
+  if (a.work_o) a.work_l = a.work_o + size_t(2) * a.n_wg * kBM * a.D;
+  const int G = a.work_o ? attn_grid(total, a.n_wg) : units;
+  a.n_wg = G;
   if (a.D == 128)
-    hipLaunchKernelGGL(window_attn_kernel<128>, grid, dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<128>, dim3(G), dim3(64 * kWaves), 0, s, a);
   else
-    hipLaunchKernelGGL(window_attn_kernel<64>, grid, dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<64>, dim3(G), dim3(64 * kWaves), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.work_o) return e;
+  if (!attn_any_split(ntiles, total, G)) return hipSuccess;   // nothing to merge
+  const int bpu = kBM / kMergeRows;
+  if (a.D == 128)
+    hipLaunchKernelGGL(window_attn_combine_kernel<128>, dim3(units * bpu), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(window_attn_combine_kernel<64>, dim3(units * bpu), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

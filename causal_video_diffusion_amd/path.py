@@ -124,6 +124,25 @@ def lowrank_apply(p: LowRank, x: torch.Tensor, y: Optional[torch.Tensor] = None,
 
 # ------------------------------------------------------------------ layer-chunk
 
+def attn_units(g: B.Geom) -> int:
+    """(head, 256-query tile) units of one chunk's attention."""
+    n_q = g.grid_h * g.grid_w * g.chunk_frames
+    return -(-n_q // 256) * g.n_heads
+
+
+def pick_attn_schedule(g: B.Geom, device=None) -> str:
+    """'split' when the chunk has more (head, query tile) units than the device
+    has compute units, else 'whole'.  With at most one unit per CU every unit
+    runs at once; splitting would only fill the idle CUs, which under a
+    power-limited clock gains less than the merge costs (measured on the
+    windowed Wan layer-chunk: 492 vs 496 µs).  With more units than CUs the
+    whole schedule needs a partly empty extra round (720p: 516 units, 256 CUs:
+    4138 vs 3040 µs)."""
+    n_cu = torch.cuda.get_device_properties(device or torch.cuda.current_device()) \
+        .multi_processor_count
+    return "split" if attn_units(g) > n_cu else "whole"
+
+
 @dataclass
 class LayerBuffers:
     """Per-call output and scratch buffers, allocated once."""
@@ -133,18 +152,35 @@ class LayerBuffers:
     t_v: Optional[torch.Tensor]
     t_o: Optional[torch.Tensor]
     lse: Optional[torch.Tensor]
+    attn_work: Optional[torch.Tensor] = None   # key-split workspace, or None
 
     @staticmethod
     def alloc(n_q: int, hidden: int, n_heads: int, rank_v: Optional[int],
-              rank_o: Optional[int], with_lse: bool = False, device="cuda"):
+              rank_o: Optional[int], with_lse: bool = False, device="cuda",
+              g: Optional[B.Geom] = None, schedule: str = "auto"):
+        """With g given, the attention schedule: "split" allocates the
+        workspace of the key-split attention (one workgroup per compute unit
+        of the current device), "whole" does not, "auto" decides by
+        pick_attn_schedule."""
         bf = dict(dtype=torch.bfloat16, device=device)
+        work = None
+        if schedule not in ("auto", "split", "whole"):
+            raise ValueError(f"schedule {schedule!r}")
+        if g is not None and schedule == "auto":
+            schedule = pick_attn_schedule(g)
+        if g is not None and schedule == "split":
+            nbytes = B.ust_window_attn_work_bytes(g, 0)
+            if nbytes <= 0:
+                raise RuntimeError("ust_window_attn_work_bytes failed")
+            work = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
         return LayerBuffers(
             v=torch.empty((n_q, hidden), **bf), o=torch.empty((n_q, hidden), **bf),
             y=torch.empty((n_q, hidden), **bf),
             t_v=torch.empty((n_q, rank_v), **bf) if rank_v else None,
             t_o=torch.empty((n_q, rank_o), **bf) if rank_o else None,
             lse=torch.empty((n_heads, n_q), dtype=torch.float32, device=device)
-            if with_lse else None)
+            if with_lse else None,
+            attn_work=work)
 
 
 def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
@@ -154,12 +190,18 @@ def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
     """One layer-chunk of the path; returns the output projection Y [NQ][H*D].
 
     x: hidden states [NQ][hidden]; q, k_new: [NQ][H*D] un-rotated (from the
-    dense query/key projections)."""
+    dense query/key projections).  The attention runs on the key-split
+    schedule when bufs holds its workspace."""
     lowrank_apply(wv, x, bufs.v, bufs.t_v)
     B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,
                     table.n_frames, frame_start)
-    B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames,
-                      frame_start, n_recent, scale, bufs.o, bufs.lse)
+    if bufs.attn_work is not None:
+        B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, table.n_frames,
+                                frame_start, n_recent, scale, bufs.o, bufs.lse,
+                                bufs.attn_work, 0)
+    else:
+        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames,
+                          frame_start, n_recent, scale, bufs.o, bufs.lse)
     lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
     return bufs.y
 

@@ -16,6 +16,8 @@
  *                         (abstract: "limiting the temporal window retained in
  *                         the attention KV cache"; chunks of three latent
  *                         frames, Table 3)
+ *   ust_window_attn_split the same attention with the work divided evenly over
+ *                         the compute units (key ranges merged afterwards)
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
  *
@@ -152,6 +154,44 @@ ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
                            int32_t n_tab_frames, int32_t frame_start,
                            int32_t n_recent, float scale, void* out,
                            float* lse_opt, hipStream_t stream);
+
+/* Bytes of device workspace that ust_window_attn_split needs when the work is
+ * divided over n_workgroups workgroups (n_workgroups <= 0: one per compute
+ * unit of the current device).  Depends only on head_dim and the workgroup
+ * count: 2 * n_workgroups * 256 * (head_dim + 1) * 4.  Returns 0 if g is
+ * invalid, n_workgroups exceeds 65536, or the device cannot be queried. */
+size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups);
+
+/* The same attention as ust_window_attn, with the same arguments, result
+ * definition and errors, scheduled for load balance.  ust_window_attn gives
+ * each (head, 256-query tile) to one workgroup, so a chunk with fewer such
+ * tiles than the device has compute units leaves units idle.  Here every
+ * (head, query tile) is a sequence of 64-key tiles, and the sequences
+ * together are cut into n_workgroups equal contiguous ranges.  A query tile
+ * whose keys fall in several ranges is finished by a second kernel, which
+ * merges the ranges' normalised partial outputs by their log-sum-exps
+ * (online softmax, merged exactly up to fp32 rounding; the output is rounded
+ * to bf16 once, after the merge).  Each part rounds its probabilities to bf16
+ * against its own running maximum, so outputs can differ from
+ * ust_window_attn's by that rounding; where no query tile is split they are
+ * identical.  It pays when a chunk has more (head, query tile) pairs than the
+ * device has compute units (a last, partly empty round of workgroups
+ * otherwise).
+ *   work: device workspace, caller-owned, at least
+ *         ust_window_attn_work_bytes(g, n_workgroups) bytes, 16-byte
+ *         aligned.  Its contents are unspecified after the call.  Calls that
+ *         share one workspace must be ordered (one stream).
+ *   n_workgroups: workgroups to divide the work over, <= 65536; <= 0 selects
+ *         one per compute unit of the current device.  Values above the
+ *         number of key tiles in the whole chunk act as that number.
+ * Errors: as ust_window_attn, plus work NULL (UST_E_NULL), misaligned
+ * (UST_E_ALIGN), work_bytes too small or n_workgroups > 65536 (UST_E_SHAPE). */
+ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void* q,
+                                 const float* cos_tab, const float* sin_tab,
+                                 int32_t n_tab_frames, int32_t frame_start,
+                                 int32_t n_recent, float scale, void* out,
+                                 float* lse_opt, void* work, size_t work_bytes,
+                                 int32_t n_workgroups, hipStream_t stream);
 
 /* Low-rank projection Y = (X A_r) B_r (+ bias) (abstract: truncated SVD of
  * the attention value and output projections).

@@ -142,24 +142,36 @@ def test_kv_append(name):
 
 # ------------------------------------------------------------------ attention
 
-def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True):
+def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True, n_wg=None):
+    """ust_window_attn, or ust_window_attn_split over n_wg workgroups (0: one
+    per compute unit) with a NaN-filled workspace, so that a merge reading a
+    partial result nobody wrote shows up as NaN."""
     q = P.to_device_bf16(qb)
     out = torch.empty_like(q)
     l = torch.empty((w.n_heads, w.n_q), dtype=torch.float32, device="cuda") if lse else None
-    B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
-                      w.n_recent if n_recent is None else n_recent, 0.0, out, l)
+    nr = w.n_recent if n_recent is None else n_recent
+    if n_wg is None:
+        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
+                          nr, 0.0, out, l)
+    else:
+        nbytes = B.ust_window_attn_work_bytes(g, n_wg)
+        assert nbytes > 0 and nbytes % 4 == 0
+        work = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
+                                nr, 0.0, out, l, work, n_wg)
     torch.cuda.synchronize()
     return P.from_device_bf16(out), (l.cpu().numpy() if lse else None)
 
 
-def _attn_case(name, full_chunks=(), rows_per_chunk=192):
+def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None):
     w = wl.ALL[name]
     for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
         qb = wl.chunk_tokens(w, wl.TAG_Q, c)
         rows = np.arange(w.n_q) if (c in full_chunks or w.n_q <= 512) else \
             _sample_rows(w.n_q, rows_per_chunk, seed=c)
-        print(f"[attn {name} chunk {c}: {len(rows)} rows]", flush=True)
-        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c)
+        mode = "" if n_wg is None else f" split over {n_wg or 'all CUs'}"
+        print(f"[attn {name}{mode} chunk {c}: {len(rows)} rows]", flush=True)
+        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
         o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
                                        w.grid_w, w.n_slots, w.n_sink, w.n_recent,
                                        rows=rows)
@@ -184,6 +196,47 @@ def test_window_attn_wan_full_cache():
 
 def test_window_attn_wan_720p():
     _attn_case("wan_720p")
+
+
+# The key-split schedule: every unit (head, 256-query tile) may be divided
+# between workgroups and merged afterwards.  n_wg = 0 is one workgroup per
+# compute unit (the benchmark's launch); the small counts make units span
+# several workgroups and workgroups span several units, with boundaries
+# inside frames and inside the ragged last key tile.
+@pytest.mark.parametrize("n_wg", [0, 1, 2, 5, 37])
+@pytest.mark.parametrize("name", ["tiny", "tiny_wrap", "mid", "mid64"])
+def test_window_attn_split_full_compare(name, n_wg):
+    _attn_case(name, n_wg=n_wg)
+
+
+def test_window_attn_split_wan_window():
+    _attn_case("wan_window", full_chunks=(5,), n_wg=0)
+
+
+def test_window_attn_split_wan_720p():
+    # 516 units: with one workgroup per CU each workgroup spans two or three units
+    _attn_case("wan_720p", n_wg=0)
+
+
+def test_window_attn_split_matches_unsplit():
+    """Where no unit is split (n_wg = units: one each; units / 2: two whole
+    units per workgroup, run one after the other) the split kernel does the
+    unsplit arithmetic exactly: bit-identical outputs.  Where units are split,
+    each part starts its own reference max, so the bf16 probabilities round
+    differently (both schedules stay within the oracle bar, tested above);
+    the log-sum-exp uses no bf16 step and agrees to fp32 rounding."""
+    w = wl.MID
+    units = -(-w.n_q // 256) * w.n_heads
+    for c, g, table, ring, cache, _, kb, vb in _append_all(w):
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        o1, l1 = _attn_gpu(g, w, ring, table, qb, c)
+        for n_wg in (units, units // 2):
+            o2, l2 = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2), f"chunk {c} n_wg {n_wg}"
+        for n_wg in (0, 3):
+            _, l2 = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
+            assert np.allclose(l1, l2, rtol=1e-5, atol=1e-5), \
+                f"chunk {c} n_wg {n_wg}: lse max diff {np.abs(l1 - l2).max():.3e}"
 
 
 def test_window_edge_cases():
@@ -218,23 +271,28 @@ def test_window_attn_longest_window_short_frames(head_dim, pairs):
         assert len(frames) == (63 if c == 20 else 128)
         print(f"[longest window D={head_dim} chunk {c}: {len(frames)} frames]", flush=True)
         qb = wl.chunk_tokens(w, wl.TAG_Q, c)
-        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c)
         o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
                                        w.grid_w, w.n_slots, w.n_sink, w.n_recent)
-        assert_close(_f64(o_gpu), o_ref, f"longest window chunk {c} O")
-        assert_close(lse_gpu, lse_ref, f"longest window chunk {c} lse", max_abs=2e-2,
-                     rel_l2=1e-3)
+        for n_wg in (None, 0, 7):
+            o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
+            assert_close(_f64(o_gpu), o_ref, f"longest window chunk {c} n_wg {n_wg} O")
+            assert_close(lse_gpu, lse_ref, f"longest window chunk {c} n_wg {n_wg} lse",
+                         max_abs=2e-2, rel_l2=1e-3)
 
 
 def test_nan_outside_window_and_determinism():
     """Poisoning every slot outside the window (and the value padding) with NaN
-    leaves the output bit-identical; two runs agree bit for bit."""
+    leaves the output bit-identical; two runs agree bit for bit.  Both
+    schedules (the split one over 5 workgroups)."""
     w = wl.MID
     for c, g, table, ring, cache, _, kb, vb in _append_all(w):
         qb = wl.chunk_tokens(w, wl.TAG_Q, c)
         o1, l1 = _attn_gpu(g, w, ring, table, qb, c)
         o2, l2 = _attn_gpu(g, w, ring, table, qb, c)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        s1, sl1 = _attn_gpu(g, w, ring, table, qb, c, n_wg=5)
+        s2, sl2 = _attn_gpu(g, w, ring, table, qb, c, n_wg=5)
+        assert np.array_equal(s1, s2) and np.array_equal(sl1, sl2)
         _, slots = O.window_slots(3 * c, 3, w.n_sink, w.n_recent, w.n_slots)
         keep_k = ring.k[slots].clone()
         keep_v = ring.v[slots].clone()
@@ -244,6 +302,8 @@ def test_nan_outside_window_and_determinism():
         ring.v[..., w.T:].view(torch.int16).fill_(NAN_BITS)
         o3, l3 = _attn_gpu(g, w, ring, table, qb, c)
         assert np.array_equal(o1, o3) and np.array_equal(l1, l3), f"chunk {c}"
+        s3, sl3 = _attn_gpu(g, w, ring, table, qb, c, n_wg=5)
+        assert np.array_equal(s1, s3) and np.array_equal(sl1, sl3), f"chunk {c} split"
         if c == 3:
             break
 
@@ -323,7 +383,8 @@ def test_layer_chunk_wan_window_chained():
     av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
     ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, w.rank)
     wv, wo = P.LowRank.from_bits(av, bv), P.LowRank.from_bits(ao, bo)
-    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank, g=g,
+                                schedule="split")
     cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
     cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
     for c in range(w.n_chunks):
@@ -381,7 +442,7 @@ def test_clip_schedule_wan_clip():
             wv=P.LowRank.from_bits(av, bv), wo=P.LowRank.from_bits(ao, bo),
             ring=P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS),
             host=(wq, wk, av, bv, ao, bo)))
-    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank, g=g)   # auto
     qbuf = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
     kbuf = torch.empty_like(qbuf)
     got = {}

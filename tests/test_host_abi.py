@@ -3,8 +3,10 @@ declares, and its host-side integer work (slot map, window plan, argument
 validation) matches the oracle bit for bit.  No kernel is launched here:
 every call below is rejected or answered on the host before any launch."""
 import ctypes
+import itertools
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -32,7 +34,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 9
+    assert len(syms) == 11
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -177,6 +179,77 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     st, msg = _raw(lib, "ust_window_attn", gp, ctypes.byref(ring10), fake, fake, fake, 21, 15,
                    6, 0.0, fake, None, None)
     assert st == "UST_E_RANGE" and "no longer in the ring" in msg
+
+
+def test_window_attn_split_rejects_bad_arguments(lib):
+    """The key-split variant validates like ust_window_attn, then its workspace;
+    every call here fails before a launch."""
+    w = wl.WAN_WINDOW
+    g = _geom(w)
+    fake = 0x10000
+    ring = B.Kv(fake, fake, 21, 3)
+    gp, rp = ctypes.byref(g), ctypes.byref(ring)
+    need = lib.ust_window_attn_work_bytes(gp, 256)
+    args = (gp, rp, fake, fake, fake, 21, 15, 6, 0.0, fake, None)
+    # the same validation as the unsplit call comes first
+    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake,
+                None, fake, need, 256, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 21, 15, 6, 0.0, None,
+                None, fake, need, 256, None)[0] == "UST_E_NULL"
+    # then the workspace
+    assert _raw(lib, "ust_window_attn_split", *args, None, need, 256, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_window_attn_split", *args, fake + 4, need, 256, None)[0] == "UST_E_ALIGN"
+    st, msg = _raw(lib, "ust_window_attn_split", *args, fake, need - 1, 256, None)
+    assert st == "UST_E_SHAPE" and "needed" in msg
+    assert _raw(lib, "ust_window_attn_split", *args, fake, need, 1 << 17, None)[0] == "UST_E_SHAPE"
+
+
+def test_window_attn_work_bytes(lib):
+    """2 partial outputs (256 rows x (D values + 1 log-sum-exp), fp32) per workgroup."""
+    for w in (wl.WAN_WINDOW, wl.TINY):
+        g = _geom(w)
+        for n in (1, 7, 256, 1000):
+            assert lib.ust_window_attn_work_bytes(ctypes.byref(g), n) == \
+                2 * n * 256 * (w.head_dim + 1) * 4
+    g = _geom(wl.WAN_WINDOW)
+    assert lib.ust_window_attn_work_bytes(ctypes.byref(g), 1 << 17) == 0
+    bad = cvd.geom(30, 52, 12, 96, 16, 16, 16, 3)
+    assert lib.ust_window_attn_work_bytes(ctypes.byref(bad), 256) == 0
+
+
+def _schedule_cases():
+    """(units, key tiles per unit, requested workgroups): the parity-test and
+    bench shapes, plus every small combination, so that units split over 1..many
+    workgroups and workgroups span 1..many units, with ragged boundaries."""
+    cases = [(228, 293, 256), (228, 293, 1), (228, 293, 228), (228, 293, 512),
+             (228, 293, 65536), (1, 3, 256), (1, 1, 256), (2, 1, 3), (19, 3, 256),
+             (19, 3, 5), (12, 500, 256), (38, 48, 256), (1000, 7, 256), (256, 10, 256),
+             (512, 10, 256), (300, 293, 256), (24, 293, 304)]
+    for u, t, g in itertools.product(range(1, 13), range(1, 13), (1, 2, 3, 5, 7, 16, 64, 1000)):
+        cases.append((u, t, g))
+    # the GPU tests' shapes: units x key tiles of every chunk, at their workgroup counts
+    shapes = [(1, (2, 3)), (2, (24, 48)), (4, (2, 4, 5)), (24, (5, 10, 15, 20)),
+              (228, (74, 147, 220, 293, 366, 439, 512)), (516, (169, 338, 507, 675, 844))]
+    for u, tiles in shapes:
+        for t in tiles:
+            for g in (1, 2, 5, 7, 37, 256, 304):
+                cases.append((u, t, g))
+    return cases
+
+
+def test_split_schedule_covers_every_tile_once(tmp_path):
+    """The key-split schedule (attn_schedule.h, shared by the attention and merge
+    kernels), run on the CPU: exact coverage, in-range key tiles and partial slots,
+    and a merge that reads exactly the slots the segments wrote."""
+    from causal_video_diffusion_amd import build
+    exe = tmp_path / "attn_schedule_check"
+    src = os.path.join(ROOT, "tests", "attn_schedule_check.cpp")
+    subprocess.run([build.hipcc(), "-O1", "-std=c++17", f"--offload-arch={build.ARCH}", src,
+                    "-o", str(exe)], check=True, capture_output=True)
+    cases = _schedule_cases()
+    inp = "".join(f"{u} {t} {g}\n" for u, t, g in cases)
+    r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == f"ok {len(cases)}", r.stdout
 
 
 def test_status_strings(lib):
