@@ -44,7 +44,10 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # written = WRITE_SIZE KiB), per (workload, schedule).  Must be re-measured
 # whenever the attention kernels change (absent = not measured for the
 # current kernels).
-ATTN_TRAFFIC_BYTES = {}
+ATTN_TRAFFIC_BYTES = {
+    ("wan_window", "whole"): (2 * 107044 + 14043) * 1024,
+    ("wan_720p", "split"): (2 * (475206 + 17007) + 58527 + 204) * 1024,   # attention + merge
+}
 
 
 def parse():
@@ -216,7 +219,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": ATTN_TRAFFIC_BYTES.get((w.name, schedule)),
-            "kernel": ("window_attn_kernel<128> + window_attn_combine_kernel<128>" if split
+            "kernel": ("window_attn_kernel<128> + window_attn_combine_kernel (one span)" if split
                        else "window_attn_kernel<128>"),
             "kernel_us": round(attn_us, 2),
         },

@@ -42,14 +42,13 @@ struct AttnArgs {
   int32_t frame_start;       // absolute frame of query token 0
   int32_t n_frames;          // frames in the window
   float qscale;              // scale * log2(e), folded into the rotated query
-  // Key-split schedule.  work_o == nullptr: one workgroup per (head, query
-  // tile).  Otherwise the (head, query tile, key tile) sequence is divided
-  // evenly over n_wg workgroups; a (head, query tile) split between
-  // workgroups leaves normalised partial outputs and their log-sum-exps here
-  // for the combine kernel.
+  // Schedule (attn_schedule.h).  work_o == nullptr: one workgroup per
+  // (head, query tile).  Otherwise the plan for n_wg workgroups; a (head,
+  // query tile) split between workgroups leaves normalised partial outputs
+  // and their log-sum-exps here for the merge kernel.
   float* work_o;             // [2 n_wg][256][D] fp32
   float* work_l;             // [2 n_wg][256] fp32 (natural log), set by the launcher
-  int32_t n_wg;              // workgroups to divide the work over (>= 1)
+  int32_t n_wg;              // requested workgroups (>= 1), set by the launcher when unsplit
   int32_t slots[UST_MAX_WINDOW_FRAMES];
 };
 

@@ -43,10 +43,10 @@
 //    robin) gets a contiguous run of (head, query tile) work: the workgroups
 //    streaming one head's K/V share an L2.
 //  * Two schedules (attn_schedule.h).  Either each workgroup owns one (head,
-//    query tile) over all key tiles, or the (head, query tile, key tile)
-//    sequence is cut into equal ranges, one per workgroup (one per CU), so a
-//    chunk with fewer query tiles than CUs still fills the chip.  A query
-//    tile split between workgroups leaves each part's normalised output and
+//    query tile) over all key tiles, or, for G workgroups, whole (head,
+//    query tile) units run G at a time and the key tiles of the remainder
+//    are cut into G equal ranges, so the last round is not partly empty.  A
+//    unit split between workgroups leaves each part's normalised output and
 //    log-sum-exp in a workspace, and a second kernel merges them.
 
 #include <type_traits>
@@ -187,11 +187,8 @@ window_attn_kernel(AttnArgs a) {
   const int ntiles = (nk + kBN - 1) / kBN;
 
   // ---- this workgroup's share of the work (attn_schedule.h) ----
-  const int G = gridDim.x;
-  const int64_t work_total = int64_t(nqt) * a.H * ntiles;
-  const int w = xcd_remap(blockIdx.x, G);
-  const int64_t x_begin = wg_range_start(w, work_total, G);
-  const int64_t x_end = wg_range_start(w + 1, work_total, G);
+  const AttnPlan plan = attn_plan(nqt * a.H, ntiles, a.n_wg);
+  const int w = xcd_remap(blockIdx.x, plan.G);
 
   // ---- per-lane constants of the tile loads ----
   // K load i of wave w fills LDS bytes [(w*KINST + i) KB, +1 KB): key row
@@ -221,16 +218,15 @@ window_attn_kernel(AttnArgs a) {
     for (int q = 0; q < 4; ++q) voffr[q] = l32 * kBN + (((2 * q + half) ^ vswz(l32)) * 8);
   }
 
-  // One segment per unit the range meets: a whole unit, or key tiles
-  // k0 .. k0+nseg-1 of one.
-  for (int64_t x = x_begin; x < x_end;) {
-    const AttnSegment sg = attn_segment(x, x_begin, x_end, w, ntiles, work_total, G);
+  // One pass per segment: a whole unit, or key tiles k0 .. k0+nseg-1 of one.
+  AttnWalk walk = attn_walk(w, plan);
+  AttnSegment sg;
+  while (attn_next(walk, w, plan, sg)) {
     const int k0 = sg.k0;
     const int nseg = sg.n;
     const int slot = sg.slot;
     const int h = sg.unit / nqt;
     const int q0 = (sg.unit % nqt) * kBM;
-    x = sg.next;
 
     __syncthreads();  // the previous segment is done with kbase / vbase
     for (int i = tid; i < a.n_frames; i += 512) {
@@ -522,25 +518,28 @@ window_attn_kernel(AttnArgs a) {
 // between workgroups.  With per-part normalised outputs O_i and log-sum-exps
 // L_i: O = sum_i e^(L_i - M) O_i / sum_i e^(L_i - M), L = M + ln sum_i
 // e^(L_i - M), M = max_i L_i, taken part by part with a running maximum.
-// One block per 64 query rows of a unit; each thread owns 4 dims of
-// kMergeRows / (256 / (D/4)) rows and keeps all of them in flight.
-constexpr int kMergeRows = 64;
-template <int D>
+// One block per ROWS query rows of a key-split unit; each thread owns 4 dims
+// of PER rows.  PER = 8 for units of a few parts (all rows of a part in
+// flight at once); PER = 1 for units of many parts, with UNR parts in flight.
+// The block first lists its unit's part slots in LDS, kMergeParts at a time.
+constexpr int kMergeParts = 256;
+template <int D, int PER>
 __global__ void __launch_bounds__(256) window_attn_combine_kernel(AttnArgs a) {
   constexpr int CPR = D / 4;                  // float4 chunks per row
   constexpr int RSTEP = 256 / CPR;            // rows apart of one thread's rows
-  constexpr int PER = kMergeRows / RSTEP;     // rows per thread
-  constexpr int BPU = kBM / kMergeRows;       // blocks per unit
+  constexpr int ROWS = RSTEP * PER;           // rows per block
+  constexpr int BPU = kBM / ROWS;             // blocks per unit
+  constexpr int UNR = PER == 1 ? 8 : 1;       // parts loaded together
+  __shared__ int part_slot[kMergeParts];
   const int nqt = (a.NQ + kBM - 1) / kBM;
   const int ntiles = (a.n_frames * a.T + kBN - 1) / kBN;
-  const int G = a.n_wg;
-  const int64_t total = int64_t(nqt) * a.H * ntiles;
-  const int u = blockIdx.x / BPU;
-  if (attn_unit_whole(u, ntiles, total, G)) return;   // written by its workgroup
-  const int64_t ue = int64_t(u + 1) * ntiles;
+  const AttnPlan plan = attn_plan(nqt * a.H, ntiles, a.n_wg);
+  const int u = plan.u0 + int(blockIdx.x) / BPU;   // only key-split units
+  if (attn_unit_whole(u, plan)) return;   // written by its workgroup
+  const int64_t ue = attn_unit_end(u, plan);
   const int h = u / nqt;
   const int c = threadIdx.x % CPR;
-  const int row0 = (blockIdx.x % BPU) * kMergeRows + threadIdx.x / CPR;
+  const int row0 = (blockIdx.x % BPU) * ROWS + threadIdx.x / CPR;
   float m[PER], sum[PER];
   float4 acc[PER];
 #pragma unroll
@@ -549,30 +548,49 @@ __global__ void __launch_bounds__(256) window_attn_combine_kernel(AttnArgs a) {
     sum[k] = 0.f;
     acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int b = attn_unit_first_wg(u, ntiles, total, G); b < G && wg_range_start(b, total, G) < ue;
-       ++b) {
-    const int slot = attn_partial_slot(b, u, ntiles, total, G);
-    const float* lp = a.work_l + int64_t(slot) * kBM;
-    const float* op = a.work_o + int64_t(slot) * kBM * D + 4 * c;
-    float l[PER];
-    float4 o[PER];
+  for (int base = attn_unit_first_wg(u, plan);
+       base < plan.G && wg_range_start(base, plan) < ue; base += kMergeParts) {
+    __syncthreads();   // the previous pass is done with part_slot
+    // workgroups base .. base+255 that start before the unit's end form a
+    // prefix (starts increase); empty ranges inside it hold no part
+    const int b = base + int(threadIdx.x);
+    const bool in_unit = b < plan.G && wg_range_start(b, plan) < ue;
+    part_slot[threadIdx.x] =
+        in_unit && attn_wg_has_part(b, plan) ? attn_partial_slot(b, u, plan) : -1;
+    const int n_listed = __syncthreads_count(in_unit);
+    for (int i = 0; i < n_listed; i += UNR) {
+      int sl[UNR];
+      float l[UNR][PER];
+      float4 o[UNR][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int row = row0 + k * RSTEP;
-      l[k] = lp[row];
-      o[k] = *reinterpret_cast<const float4*>(op + int64_t(row) * D);
-    }
+      for (int j = 0; j < UNR; ++j) {
+        sl[j] = i + j < n_listed ? part_slot[i + j] : -1;
+        if (sl[j] < 0) continue;
+        const float* lp = a.work_l + int64_t(sl[j]) * kBM;
+        const float* op = a.work_o + int64_t(sl[j]) * kBM * D + 4 * c;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const float mn = fmaxf(m[k], l[k]);
-      const float sa = expf(m[k] - mn);   // 0 on the first part (m = -inf)
-      const float e = expf(l[k] - mn);
-      m[k] = mn;
-      sum[k] = sum[k] * sa + e;
-      acc[k].x = acc[k].x * sa + e * o[k].x;
-      acc[k].y = acc[k].y * sa + e * o[k].y;
-      acc[k].z = acc[k].z * sa + e * o[k].z;
-      acc[k].w = acc[k].w * sa + e * o[k].w;
+        for (int k = 0; k < PER; ++k) {
+          const int row = row0 + k * RSTEP;
+          l[j][k] = lp[row];
+          o[j][k] = *reinterpret_cast<const float4*>(op + int64_t(row) * D);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        if (sl[j] < 0) continue;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const float mn = fmaxf(m[k], l[j][k]);
+          const float sa = expf(m[k] - mn);   // 0 on the first part (m = -inf)
+          const float e = expf(l[j][k] - mn);
+          m[k] = mn;
+          sum[k] = sum[k] * sa + e;
+          acc[k].x = acc[k].x * sa + e * o[j][k].x;
+          acc[k].y = acc[k].y * sa + e * o[j][k].y;
+          acc[k].z = acc[k].z * sa + e * o[j][k].z;
+          acc[k].w = acc[k].w * sa + e * o[j][k].w;
+        }
+      }
     }
   }
 #pragma unroll
@@ -599,24 +617,32 @@ hipError_t launch_window_attn(const AttnArgs& args, hipStream_t s) {
   const int nqt = (a.NQ + kBM - 1) / kBM;
   const int units = nqt * a.H;
   const int ntiles = (a.n_frames * a.T + kBN - 1) / kBN;
-  const int64_t total = int64_t(units) * ntiles;
-  // one workgroup per unit, or the requested count (at most one per step);
-  // the workspace is laid out for the requested count
+  // one workgroup per unit, or the plan for the requested count; the
+  // workspace is laid out for the requested count (slots < 2 G <= 2 n_wg)
   if (a.work_o) a.work_l = a.work_o + size_t(2) * a.n_wg * kBM * a.D;
-  const int G = a.work_o ? attn_grid(total, a.n_wg) : units;
-  a.n_wg = G;
+  else a.n_wg = units;
+  const AttnPlan plan = attn_plan(units, ntiles, a.n_wg);
   if (a.D == 128)
-    hipLaunchKernelGGL(window_attn_kernel<128>, dim3(G), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<128>, dim3(plan.G), dim3(64 * kWaves), 0, s, a);
   else
-    hipLaunchKernelGGL(window_attn_kernel<64>, dim3(G), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL(window_attn_kernel<64>, dim3(plan.G), dim3(64 * kWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.work_o) return e;
-  if (!attn_any_split(ntiles, total, G)) return hipSuccess;   // nothing to merge
-  const int bpu = kBM / kMergeRows;
-  if (a.D == 128)
-    hipLaunchKernelGGL(window_attn_combine_kernel<128>, dim3(units * bpu), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(window_attn_combine_kernel<64>, dim3(units * bpu), dim3(256), 0, s, a);
+  if (!attn_any_split(plan)) return hipSuccess;   // nothing to merge
+  // Parts per split unit: about ntiles / (steps per range) + 2.  Few: one
+  // block per 64 rows (8 per thread); many: one block per 256 / (D / 4) rows
+  // with several parts in flight.
+  const int split_units = units - plan.u0;
+  const bool many = plan.steps / plan.G * 4 < ntiles;
+  const int rows = (256 / (a.D / 4)) * (many ? 1 : 8);
+  const dim3 grid(split_units * (kBM / rows));
+  if (a.D == 128) {
+    if (many) hipLaunchKernelGGL((window_attn_combine_kernel<128, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((window_attn_combine_kernel<128, 8>), grid, dim3(256), 0, s, a);
+  } else {
+    if (many) hipLaunchKernelGGL((window_attn_combine_kernel<64, 1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((window_attn_combine_kernel<64, 8>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

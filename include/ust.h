@@ -17,7 +17,7 @@
  *                         the attention KV cache"; chunks of three latent
  *                         frames, Table 3)
  *   ust_window_attn_split the same attention with the work divided evenly over
- *                         the compute units (key ranges merged afterwards)
+ *                         the workgroups (split key ranges merged afterwards)
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
  *
@@ -164,19 +164,19 @@ size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups);
 
 /* The same attention as ust_window_attn, with the same arguments, result
  * definition and errors, scheduled for load balance.  ust_window_attn gives
- * each (head, 256-query tile) to one workgroup, so a chunk with fewer such
- * tiles than the device has compute units leaves units idle.  Here every
- * (head, query tile) is a sequence of 64-key tiles, and the sequences
- * together are cut into n_workgroups equal contiguous ranges.  A query tile
- * whose keys fall in several ranges is finished by a second kernel, which
- * merges the ranges' normalised partial outputs by their log-sum-exps
- * (online softmax, merged exactly up to fp32 rounding; the output is rounded
- * to bf16 once, after the merge).  Each part rounds its probabilities to bf16
- * against its own running maximum, so outputs can differ from
- * ust_window_attn's by that rounding; where no query tile is split they are
- * identical.  It pays when a chunk has more (head, query tile) pairs than the
- * device has compute units (a last, partly empty round of workgroups
- * otherwise).
+ * each (head, 256-query tile) pair (a unit) to one workgroup, so a chunk
+ * whose unit count is not a multiple of the device's compute units leaves
+ * units idle in its last round.  Here, with G = n_workgroups: the first
+ * floor(U / G) * G of the U units run whole, G at a time; the key tiles of
+ * the other units, unit after unit, are cut into G equal contiguous ranges,
+ * one per workgroup.  A unit whose keys fall in several ranges is finished
+ * by a second kernel, which merges the ranges' normalised partial outputs by
+ * their log-sum-exps (online softmax, merged exactly up to fp32 rounding;
+ * the output is rounded to bf16 once, after the merge).  Each part rounds its
+ * probabilities to bf16 against its own running maximum, so outputs can
+ * differ from ust_window_attn's by that rounding; where no unit is split
+ * they are identical.  It pays when U exceeds the compute-unit count and is
+ * not a multiple of it (a last, partly empty round otherwise).
  *   work: device workspace, caller-owned, at least
  *         ust_window_attn_work_bytes(g, n_workgroups) bytes, 16-byte
  *         aligned.  Its contents are unspecified after the call.  Calls that

@@ -1,15 +1,17 @@
-// Host check of the key-split attention schedule (attn_schedule.h), built
-// and run by test_host_abi.py on the CPU.  Reads lines "n_units ntiles G"
-// (G = the requested workgroup count) and checks, for each:
+// Host check of the attention schedule (attn_schedule.h), built and run by
+// test_host_abi.py on the CPU.  Reads lines "n_units ntiles G" (G = the
+// requested workgroup count) and checks, for each plan:
 //  - every (unit, key tile) is computed by exactly one segment;
-//  - every segment lies inside its unit's key tiles (no wrap, no overrun)
-//    and inside its workgroup's range;
-//  - partial slots are < 2 G and used once; a unit is whole (written
-//    directly, slot -1) exactly when the merge skips it;
+//  - every segment lies inside its unit's key tiles (no wrap, no overrun);
+//  - whole-unit rounds come first and give round k's unit k * G + w to
+//    workgroup w; key-split segments lie in their workgroup's range;
+//  - partial slots are < 2 G, belong to their workgroup and are used once;
+//    a unit is whole (written directly, slot -1) exactly when the merge
+//    skips it;
 //  - the merge enumerates, for each split unit, exactly the slots that its
 //    segments wrote;
 //  - the merge is launched exactly when some unit is split.
-// Prints "ok" per line, or the first violation and exits 1.
+// Prints "ok <count>", or the first violation and exits 1.
 #include <cstdio>
 #include <cstdlib>
 #include <set>
@@ -25,45 +27,53 @@ static int fail(const char* what, long a, long b, long c) {
 }
 
 static int check(int units, int ntiles, int requested) {
-  const int64_t total = int64_t(units) * ntiles;
-  const int G = attn_grid(total, requested);
-  if (G < 1 || G > requested) return fail("grid", units, ntiles, requested);
-  std::vector<int> cover(size_t(total), 0);
+  const AttnPlan p = attn_plan(units, ntiles, requested);
+  if (p.G < 1 || p.G > requested) return fail("grid", units, ntiles, requested);
+  if (p.u0 != p.q * p.G || p.u0 > units || (units >= requested && units - p.u0 >= p.G))
+    return fail("rounds", units, p.q, p.G);
+  if (p.steps != int64_t(units - p.u0) * ntiles) return fail("steps", units, ntiles, long(p.steps));
+  std::vector<int> cover(size_t(units) * ntiles, 0);
   std::vector<std::set<int>> written(units);   // partial slots per unit
   std::vector<int> whole_writes(units, 0);
   std::set<int> used;
-  for (int w = 0; w < G; ++w) {
-    const int64_t xb = wg_range_start(w, total, G), xe = wg_range_start(w + 1, total, G);
-    if (xe <= xb) return fail("empty range", units, ntiles, w);
-    int segs = 0;
-    for (int64_t x = xb; x < xe;) {
-      const AttnSegment s = attn_segment(x, xb, xe, w, ntiles, total, G);
-      if (s.next <= x || s.next > xe) return fail("segment end", w, long(x), long(s.next));
-      if (s.unit < 0 || s.unit >= units) return fail("unit", w, s.unit, units);
-      if (s.n != s.next - x || s.n < 1) return fail("length", w, s.n, long(s.next - x));
-      if (s.k0 < 0 || s.k0 + s.n > ntiles) return fail("key range", w, s.k0, s.n);
-      if (int64_t(s.unit) * ntiles > x || int64_t(s.unit + 1) * ntiles < s.next)
-        return fail("segment outside its unit", w, s.unit, long(x));
-      for (int k = s.k0; k < s.k0 + s.n; ++k) ++cover[size_t(int64_t(s.unit) * ntiles + k)];
-      if (s.slot < 0) {
-        if (s.n != ntiles) return fail("partial without slot", w, s.unit, s.n);
-        ++whole_writes[s.unit];
+  for (int w = 0; w < p.G; ++w) {
+    AttnWalk s = attn_walk(w, p);
+    AttnSegment g;
+    int k = 0;
+    int64_t x = s.xb;
+    while (attn_next(s, w, p, g)) {
+      if (g.unit < 0 || g.unit >= units) return fail("unit", w, g.unit, units);
+      if (g.n < 1 || g.k0 < 0 || g.k0 + g.n > ntiles) return fail("key range", w, g.k0, g.n);
+      if (k < p.q) {
+        if (g.unit != k * p.G + w || g.k0 != 0 || g.n != ntiles || g.slot != -1)
+          return fail("whole round", w, k, g.unit);
+        ++k;
       } else {
-        if (s.slot >= 2 * G) return fail("slot range", w, s.slot, G);
-        if (!used.insert(s.slot).second) return fail("slot reused", w, s.slot, s.unit);
-        if (s.slot / 2 != w) return fail("slot owner", w, s.slot, s.unit);
-        written[s.unit].insert(s.slot);
+        // a key-split segment: steps [x, x + n) of this workgroup's range
+        if (g.unit < p.u0) return fail("split unit in rounds", w, g.unit, p.u0);
+        const int64_t ub = int64_t(g.unit - p.u0) * ntiles;
+        if (x < ub || x + g.n > ub + ntiles || x + g.n > s.xe)
+          return fail("segment outside range", w, g.unit, long(x));
+        x += g.n;
       }
-      x = s.next;
-      ++segs;
+      for (int t = g.k0; t < g.k0 + g.n; ++t) ++cover[size_t(g.unit) * ntiles + t];
+      if (g.slot < 0) {
+        if (g.n != ntiles) return fail("partial without slot", w, g.unit, g.n);
+        ++whole_writes[g.unit];
+      } else {
+        if (g.slot >= 2 * p.G) return fail("slot range", w, g.slot, p.G);
+        if (!used.insert(g.slot).second) return fail("slot reused", w, g.slot, g.unit);
+        if (g.slot / 2 != w) return fail("slot owner", w, g.slot, g.unit);
+        written[g.unit].insert(g.slot);
+      }
     }
-    if (segs < 1) return fail("no segment", units, ntiles, w);
+    if (k != p.q || x != s.xe) return fail("walk incomplete", w, k, long(x));
   }
-  for (int64_t i = 0; i < total; ++i)
-    if (cover[size_t(i)] != 1) return fail("coverage", long(i / ntiles), long(i % ntiles), cover[size_t(i)]);
+  for (size_t i = 0; i < cover.size(); ++i)
+    if (cover[i] != 1) return fail("coverage", long(i / ntiles), long(i % ntiles), cover[i]);
   bool any = false;
   for (int u = 0; u < units; ++u) {
-    const bool whole = attn_unit_whole(u, ntiles, total, G);
+    const bool whole = attn_unit_whole(u, p);
     if (whole != (whole_writes[u] == 1)) return fail("whole flag", u, whole, whole_writes[u]);
     if (whole) {
       if (!written[u].empty()) return fail("whole unit with partials", u, 0, 0);
@@ -71,12 +81,12 @@ static int check(int units, int ntiles, int requested) {
     }
     any = true;
     std::set<int> merged;
-    const int64_t ue = int64_t(u + 1) * ntiles;
-    for (int b = attn_unit_first_wg(u, ntiles, total, G); b < G && wg_range_start(b, total, G) < ue; ++b)
-      merged.insert(attn_partial_slot(b, u, ntiles, total, G));
+    const int64_t ue = attn_unit_end(u, p);
+    for (int b = attn_unit_first_wg(u, p); b < p.G && wg_range_start(b, p) < ue; ++b)
+      if (attn_wg_has_part(b, p)) merged.insert(attn_partial_slot(b, u, p));
     if (merged != written[u]) return fail("merge slots", u, long(merged.size()), long(written[u].size()));
   }
-  if (any != attn_any_split(ntiles, total, G)) return fail("any split", units, ntiles, G);
+  if (any != attn_any_split(p)) return fail("any split", units, ntiles, p.G);
   return 0;
 }
 

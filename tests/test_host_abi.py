@@ -224,7 +224,10 @@ def _schedule_cases():
     cases = [(228, 293, 256), (228, 293, 1), (228, 293, 228), (228, 293, 512),
              (228, 293, 65536), (1, 3, 256), (1, 1, 256), (2, 1, 3), (19, 3, 256),
              (19, 3, 5), (12, 500, 256), (38, 48, 256), (1000, 7, 256), (256, 10, 256),
-             (512, 10, 256), (300, 293, 256), (24, 293, 304)]
+             (512, 10, 256), (300, 293, 256), (24, 293, 304),
+             # whole-unit rounds followed by a small key-split rest
+             (516, 844, 256), (257, 1, 256), (300, 2, 256), (4, 1, 3), (513, 3, 256),
+             (1000, 1, 999), (600, 5, 256)]
     for u, t, g in itertools.product(range(1, 13), range(1, 13), (1, 2, 3, 5, 7, 16, 64, 1000)):
         cases.append((u, t, g))
     # the GPU tests' shapes: units x key tiles of every chunk, at their workgroup counts
