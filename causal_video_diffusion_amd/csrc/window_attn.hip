@@ -237,6 +237,9 @@ window_attn_kernel(AttnArgs a) {
     // ---- query fragments: RoPE at the query's own position, scale, bf16 ----
     const int qn = q0 + wave * 32 + l32;
     const bool qvalid = qn < a.NQ;
+    // a wave whose queries all lie past the chunk (in a head's last, ragged
+    // query tile) only loads its share of the tiles and keeps the barriers
+    const bool wave_busy = q0 + wave * 32 < a.NQ;
     bf16x8 qf[KS];
     {
       const uint16_t* qp = a.q + (int64_t(qn) * a.H + h) * D;
@@ -448,8 +451,8 @@ window_attn_kernel(AttnArgs a) {
     const int lead = group_a ? 2 : 3;
     auto step = [&](int j, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(2);
-      if (j < nseg) qk(cur);       // first, so its scores are ready for softmax(j)
-      if (j >= 1) pv(prev);
+      if (j < nseg && wave_busy) qk(cur);   // first, so its scores are ready for softmax(j)
+      if (j >= 1 && wave_busy) pv(prev);
       __builtin_amdgcn_s_setprio(0);
       barrier();
       const int v = j + lead;      // tile this wave requests now
@@ -457,7 +460,7 @@ window_attn_kernel(AttnArgs a) {
         if (group_a) issue(k0 + v, st2);
         else issue(k0 + v, st3);
       }
-      if (j < nseg) softmax(j);
+      if (j < nseg && wave_busy) softmax(j);
       if (v < nseg) wait_vmcnt<NLD>();   // own share of tile v-1 landed
       else wait_vmcnt<0>();
       barrier();
