@@ -53,9 +53,11 @@ ATTN_TRAFFIC_BYTES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("wan_window", "wan_720p"), default="wan_window",
-                    help="layer-chunk shape: the windowed Wan2.1-1.3B layer (default), or "
-                         "the same layer at 720p (45x80 tokens/frame, rank 256)")
+    ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip"),
+                    default="wan_window",
+                    help="the windowed Wan2.1-1.3B layer-chunk (default); the same layer "
+                         "at 720p (45x80 tokens/frame, rank 256); or the whole 81-frame "
+                         "clip schedule over 30 layers (a step is then one clip)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -93,6 +95,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.load()
     torch.cuda.set_device(0)
+    if args.workload == "wan_clip":
+        return main_clip(args)
     w = wl.ALL[args.workload]
     C = 5                                   # steady-state chunk
     F0 = 3 * C
@@ -237,6 +241,155 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, C, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+def main_clip(args):
+    """The 81-frame clip (UnStep, Table 3): 7 chunks of 3 latent frames; chunk
+    0 runs 4 denoising forwards and each later chunk 2, every chunk one more
+    clean-cache forward; 23 forwards x 30 layers = 690 layer-chunks, each
+    with its own weights and KV ring, in one stream.  Per layer-chunk: dense
+    Q and K projections (harness support, reported apart), then the path.
+    A step is one whole clip."""
+    import numpy as np
+    import torch
+
+    import causal_video_diffusion_amd as cvd
+    from causal_video_diffusion_amd import _binding as B
+    from causal_video_diffusion_amd import path as P
+    from causal_video_diffusion_amd import workload as wl
+
+    w = wl.WAN_CLIP
+    g = cvd.geom(*w.geom_tuple())
+    stream = torch.cuda.current_stream()
+    sched = P.clip_forwards(w.n_chunks, w.first_steps, w.later_steps, w.clean_pass)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    layers = []
+    for layer in range(w.layers):
+        if layer % 10 == 0:
+            print(f"[bench clip] preparing layer {layer} of {w.layers}", file=sys.stderr, flush=True)
+        av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank, layer)
+        ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, w.rank, layer)
+        layers.append(dict(
+            wq=P.LowRank(P.to_device_bf16(P.output_major(wl.dense_weight_bf16(w, wl.TAG_WQ, layer))), None),
+            wk=P.LowRank(P.to_device_bf16(P.output_major(wl.dense_weight_bf16(w, wl.TAG_WK, layer))), None),
+            wv=P.LowRank.from_bits(av, bv), wo=P.LowRank.from_bits(ao, bo),
+            ring=P.Ring(g, w.n_slots, w.n_sink, fill_bits=0x7FC1)))
+    xs = [P.to_device_bf16(wl.activations(w, c, s)) for (c, s, _) in sched]
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, w.rank, w.rank, g=g)
+    schedule = "split" if bufs.attn_work is not None else "whole"
+    qbuf = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    kbuf = torch.empty_like(qbuf)
+    # attention flops of every layer-chunk (window sizes from the host plan)
+    n_keys = [len(B.ust_window_plan(g, layers[0]["ring"].abi, 3 * c, w.n_recent)[0]) * w.T
+              for (c, _, _) in sched]
+    flops = sum(w.layers * attn_flops(w.n_q, nk, w.head_dim, w.n_heads) for nk in n_keys)
+    n_lc = len(sched) * w.layers
+
+    def attention(ring, c):
+        if bufs.attn_work is not None:
+            B.ust_window_attn_split(g, ring.abi, qbuf, table.cos, table.sin, w.n_tab_frames,
+                                    3 * c, w.n_recent, 0.0, bufs.o, None, bufs.attn_work, 0)
+        else:
+            B.ust_window_attn(g, ring.abi, qbuf, table.cos, table.sin, w.n_tab_frames, 3 * c,
+                              w.n_recent, 0.0, bufs.o, None)
+
+    # ev: None, or a list that receives 4 events per layer-chunk: before the
+    # Q/K projections, before the path, around the attention
+    def clip(ev=None):
+        for fi, (c, _, _) in enumerate(sched):
+            x = xs[fi]
+            for L in layers:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if ev is not None else None
+                if e:
+                    e[0].record(stream)
+                P.lowrank_apply(L["wq"], x, qbuf)
+                P.lowrank_apply(L["wk"], x, kbuf)
+                if e:
+                    e[1].record(stream)
+                P.lowrank_apply(L["wv"], x, bufs.v, bufs.t_v)
+                B.ust_kv_append(g, L["ring"].abi, kbuf, bufs.v, table.cos, table.sin,
+                                w.n_tab_frames, 3 * c)
+                if e:
+                    e[2].record(stream)
+                attention(L["ring"], c)
+                if e:
+                    e[3].record(stream)
+                P.lowrank_apply(L["wo"], bufs.o, bufs.y, bufs.t_o)
+                if e:
+                    e[4].record(stream)
+                    ev.append(e)
+
+    print("[bench clip] warm-up", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        clip()
+    torch.cuda.synchronize()
+    print("[bench clip] timing", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        clip()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    clip_ms = t0.elapsed_time(t1) / args.steps
+    # split of one clip, outside the timed region (events add ~2-3 us each)
+    evs = []
+    clip(evs)
+    torch.cuda.synchronize()
+    qk_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    path_ms = sum(e[1].elapsed_time(e[4]) for e in evs)
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (clip_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(clip_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"wan_clip: 81-frame clip = {w.n_chunks} chunks x 3 latent frames, "
+                        f"{len(sched)} forwards (4 + 2 per later chunk, + 1 clean-cache "
+                        f"forward per chunk) x {w.layers} layers = {n_lc} layer-chunks; each "
+                        f"Wan2.1-1.3B self-attention layer-chunk with dense Q/K projections, "
+                        f"rank-{w.rank} V/O, window {w.n_sink} sink + {w.n_recent} recent + 3 "
+                        f"current frames, {w.n_slots}-slot ring per layer; a step is one clip",
+            "layer_chunks": n_lc, "attn_tflop_per_clip": round(flops / 1e12, 2),
+            "schedule": schedule,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "window_attn_kernel<128>, all 690 launches of one clip",
+            "kernel_ms_per_clip": round(attn_ms, 3),
+        },
+        "clip_ms": round(clip_ms, 3),
+        "layer_chunk_us_mean": round(1000.0 * clip_ms / n_lc, 2),
+        "split_ms": {"qk_dense_proj": round(qk_ms, 3), "path": round(path_ms, 3),
+                     "attention": round(attn_ms, 3)},
+        "split_note": "one clip in a separate pass with events around each layer-chunk's "
+                      "Q/K projections, its path (V projection, append, attention, O "
+                      "projection) and its attention; events add ~2-3 us each",
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl.WAN_WINDOW, 5, args.cpu_reps)
+        rate = cb["value"] * 1e12               # oracle attention flop/s, steady layer-chunk
+        cb["extrapolated_clip_s"] = round(flops / rate, 1)
+        cb["sample"] = ("one steady-state layer-chunk of the clip's shape (the wan_window "
+                        "layer-chunk), whole, timed; the clip's time is extrapolated from it "
+                        "by attention flops over the 690 layer-chunks. " + cb["sample"])
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
