@@ -189,6 +189,22 @@ def main():
     names = ["v_proj_us", "rope_k_append_us", "window_attn_us", "o_proj_us"]
     stage = {n: 1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs]))
              for i, n in enumerate(names)}
+    # the append from HBM: reading 512 MiB before each rep evicts its inputs
+    # from L2 and the 256 MB MALL (a read leaves no dirty lines behind whose
+    # write-back the append would pay for); events around the append alone
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(20):
+        flush.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(1000.0 * e0.elapsed_time(e1))
+    del flush
+    stage["rope_k_append_cold_us"] = float(np.median(cold))
     attn_tflops = flops / (attn_us * 1e-6) / 1e12
     append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
     lowrank_flops = 2 * 2.0 * w.n_q * w.hidden * w.rank
@@ -229,11 +245,15 @@ def main():
         },
         "stages_us": {k: round(v, 2) for k, v in stage.items()},
         "stages_note": "separate untimed pass with an event between every stage "
-                       "(each event adds ~2-3 us; stage times include launch gaps)",
+                       "(each event adds ~2-3 us; stage times include launch gaps); "
+                       "rope_k_append_cold_us: the append alone after reading 512 MiB, "
+                       "median of 20",
         "stages": {
             "rope_k_append_GBs": round(append_bytes / (stage["rope_k_append_us"] * 1e-6) / 1e9, 1),
             "rope_k_append_hbm_frac": round(append_bytes / (stage["rope_k_append_us"] * 1e-6)
                                             / 1e9 / PEAK_HBM_GBS, 4),
+            "rope_k_append_cold_hbm_frac": round(append_bytes / (stage["rope_k_append_cold_us"]
+                                                                 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "lowrank_v_o_TFLOPs": round(lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"])
                                                          * 1e-6) / 1e12, 1),
         },

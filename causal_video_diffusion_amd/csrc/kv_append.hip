@@ -10,8 +10,9 @@
 //           of 8 consecutive tokens per dimension into the transposed value
 //           slot [slot][h][dim][t] (the layout the attention's PV product
 //           reads without a transpose).
-// The work is a streaming copy with no reuse (HBM-bound); the table rows are
-// re-read by every head from L2.
+// The work is a streaming copy with no reuse (HBM-bound).  Workgroups are
+// ordered head-fastest and XCD-aware, so the table rows of a token tile are
+// fetched from HBM once and re-read by its other heads from the same L2.
 
 #include "ust_device.h"
 #include "ust_internal.h"
@@ -21,39 +22,65 @@ namespace {
 
 constexpr int kTok = 64;  // tokens per workgroup
 
+// map blockIdx to work so each XCD (8, dispatched round robin) gets a
+// contiguous range: the heads of one token tile then share an L2 and the
+// tile's table rows are fetched from HBM once
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb / 8, rem = nb % 8;
+  const int x = b % 8, k = b / 8;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256)
 kv_append_kernel(AppendArgs a) {
   constexpr int P = D / 2;
   constexpr int CH = D / 8;          // 16-byte chunks per head row
   constexpr int LROW = D / 2 + 1;    // LDS row stride in dwords (padded)
+  constexpr int IT = (kTok * CH) / 256;
   __shared__ uint32_t vt[kTok * LROW];
 
   const int ntile = (a.T + kTok - 1) / kTok;
-  const int fi = blockIdx.x / ntile;             // frame within the chunk
-  const int t0 = (blockIdx.x % ntile) * kTok;    // first token of the tile
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = w % a.H;                         // head fastest: one tile's heads are adjacent
+  const int tile = w / a.H;
+  const int fi = tile / ntile;                   // frame within the chunk
+  const int t0 = (tile % ntile) * kTok;          // first token of the tile
   const int nt = min(kTok, a.T - t0);            // tokens here, a multiple of 8
-  const int h = blockIdx.y;
   const int slot = a.chunk_slot[fi];
   const int64_t row0 = int64_t(fi) * a.T + t0;   // chunk token index of t0
   const int64_t tab0 = (int64_t(a.frame_start) * a.T + row0) * P;
+  const uint16_t* __restrict__ knew = a.k_new;
+  const uint16_t* __restrict__ vnew = a.v_new;
+  const float* __restrict__ ctab = a.cos_tab;
+  const float* __restrict__ stab = a.sin_tab;
+
+  // all loads first (nothing is stored before them, so they are in flight
+  // together), then rotation and stores
+  uint4 kw[IT], vw[IT];
+  float4 cs[IT], sn[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = threadIdx.x + 256 * it;
+    const int tl = min(c / CH, nt - 1);          // rows past the frame re-read the last one
+    const int dc = c % CH;
+    const int64_t src = ((row0 + tl) * a.H + h) * D + dc * 8;
+    kw[it] = *reinterpret_cast<const uint4*>(knew + src);
+    vw[it] = *reinterpret_cast<const uint4*>(vnew + src);
+    cs[it] = *reinterpret_cast<const float4*>(ctab + tab0 + int64_t(tl) * P + dc * 4);
+    sn[it] = *reinterpret_cast<const float4*>(stab + tab0 + int64_t(tl) * P + dc * 4);
+  }
 
   uint16_t* kdst = a.k_cache + ((int64_t(slot) * a.H + h) * a.T + t0) * D;
-
 #pragma unroll
-  for (int it = 0; it < (kTok * CH) / 256; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int c = threadIdx.x + 256 * it;
     const int tl = c / CH;
     const int dc = c % CH;
     if (tl < nt) {
-      const int64_t src = ((row0 + tl) * a.H + h) * D + dc * 8;
-      const uint4 kw = *reinterpret_cast<const uint4*>(a.k_new + src);
-      const uint4 vw = *reinterpret_cast<const uint4*>(a.v_new + src);
-      const float4 cs = *reinterpret_cast<const float4*>(a.cos_tab + tab0 + int64_t(tl) * P + dc * 4);
-      const float4 sn = *reinterpret_cast<const float4*>(a.sin_tab + tab0 + int64_t(tl) * P + dc * 4);
-      const uint32_t kin[4] = {kw.x, kw.y, kw.z, kw.w};
-      const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
-      const float s4[4] = {sn.x, sn.y, sn.z, sn.w};
+      const uint32_t kin[4] = {kw[it].x, kw[it].y, kw[it].z, kw[it].w};
+      const float c4[4] = {cs[it].x, cs[it].y, cs[it].z, cs[it].w};
+      const float s4[4] = {sn[it].x, sn[it].y, sn[it].z, sn[it].w};
       uint32_t kout[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -64,10 +91,10 @@ kv_append_kernel(AppendArgs a) {
       *reinterpret_cast<uint4*>(kdst + int64_t(tl) * D + dc * 8) =
           make_uint4(kout[0], kout[1], kout[2], kout[3]);
       uint32_t* row = vt + tl * LROW + dc * 4;
-      row[0] = vw.x;
-      row[1] = vw.y;
-      row[2] = vw.z;
-      row[3] = vw.w;
+      row[0] = vw[it].x;
+      row[1] = vw[it].y;
+      row[2] = vw[it].z;
+      row[3] = vw[it].w;
     }
   }
   __syncthreads();
@@ -81,14 +108,14 @@ kv_append_kernel(AppendArgs a) {
     const int tg = c % (kTok / 8);
     const int d = c / (kTok / 8);
     if (tg * 8 < nt) {
-      uint32_t w[4];
+      uint32_t wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t lo = vt16[(tg * 8 + 2 * e) * (2 * LROW) + d];
         const uint32_t hi = vt16[(tg * 8 + 2 * e + 1) * (2 * LROW) + d];
-        w[e] = lo | (hi << 16);
+        wv[e] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(vdst + int64_t(d) * a.TV + tg * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(vdst + int64_t(d) * a.TV + tg * 8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
   }
 }
@@ -97,7 +124,7 @@ kv_append_kernel(AppendArgs a) {
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
   const int ntile = (a.T + kTok - 1) / kTok;
-  dim3 grid(ntile * a.C, a.H);
+  dim3 grid(ntile * a.C * a.H);
   if (a.D == 128)
     hipLaunchKernelGGL(kv_append_kernel<128>, grid, dim3(256), 0, s, a);
   else
