@@ -53,11 +53,13 @@ ATTN_TRAFFIC_BYTES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip"),
+    ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip", "wan_fused"),
                     default="wan_window",
                     help="the windowed Wan2.1-1.3B layer-chunk (default); the same layer "
-                         "at 720p (45x80 tokens/frame, rank 256); or the whole 81-frame "
-                         "clip schedule over 30 layers (a step is then one clip)")
+                         "at 720p (45x80 tokens/frame, rank 256); the whole 81-frame "
+                         "clip schedule over 30 layers (a step is then one clip); or the "
+                         "windowed layer-chunk with the fused Q/K/V projection and the "
+                         "pages' rank 1413, re-densified")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,6 +99,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "wan_clip":
         return main_clip(args)
+    if args.workload == "wan_fused":
+        return main_fused(args)
     w = wl.ALL[args.workload]
     C = 5                                   # steady-state chunk
     F0 = 3 * C
@@ -261,6 +265,125 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, C, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+def main_fused(args):
+    """The windowed Wan layer-chunk (chunk 5, steady state) with the fused
+    projection: one product X [W_q | W_k | W_v]^T whose epilogue rotates K
+    and appends K and V to the ring (ust_qkv_append), the attention, and the
+    output projection.  V and O use the pages' SVD rank 1413 (0.92 x 1536),
+    above the 768 break-even, so both run dense with W_r = A_r B_r
+    re-densified once.  Unlike the default step, this one includes the Q and
+    K projections."""
+    import numpy as np
+    import torch
+
+    import causal_video_diffusion_amd as cvd
+    from causal_video_diffusion_amd import _binding as B
+    from causal_video_diffusion_amd import path as P
+    from causal_video_diffusion_amd import workload as wl
+
+    w = wl.WAN_WINDOW
+    C, F0, rank = 5, 15, 1413
+    g = cvd.geom(*w.geom_tuple())
+    stream = torch.cuda.current_stream()
+    av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, rank)
+    ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, rank)
+    w_qkv = P.qkv_weights(wl.dense_weight_bf16(w, wl.TAG_WQ), wl.dense_weight_bf16(w, wl.TAG_WK),
+                          P.densify(av, bv))
+    wo = P.LowRank(P.densify(ao, bo), None)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=0x7FC1)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, None, None, g=g)
+    schedule = "split" if bufs.attn_work is not None else "whole"
+    qbuf = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    xs = [P.to_device_bf16(wl.activations(w, c)) for c in range(C + 1)]
+    for c in range(C):
+        P.layer_chunk_fused(g, ring, table, xs[c], w_qkv, wo, 3 * c, w.n_recent, bufs, qbuf)
+    torch.cuda.synchronize()
+    x = xs[C]
+    n_k = len(B.ust_window_plan(g, ring.abi, F0, w.n_recent)[0]) * w.T
+    flops = attn_flops(w.n_q, n_k, w.head_dim, w.n_heads)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.ust_qkv_append(g, ring.abi, x, w_qkv, w.hidden, table.cos, table.sin, w.n_tab_frames,
+                         F0, qbuf)
+        if ev is not None:
+            ev[1].record(stream)
+        if bufs.attn_work is not None:
+            B.ust_window_attn_split(g, ring.abi, qbuf, table.cos, table.sin, w.n_tab_frames, F0,
+                                    w.n_recent, 0.0, bufs.o, None, bufs.attn_work, 0)
+        else:
+            B.ust_window_attn(g, ring.abi, qbuf, table.cos, table.sin, w.n_tab_frames, F0,
+                              w.n_recent, 0.0, bufs.o, None)
+        if ev is not None:
+            ev[2].record(stream)
+        P.lowrank_apply(wo, bufs.o, bufs.y)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in sevs:
+        step(e)
+    torch.cuda.synchronize()
+    names = ["qkv_proj_rope_k_append_us", "window_attn_us", "o_proj_us"]
+    stage = {n: round(1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs])), 2)
+             for i, n in enumerate(names)}
+    attn_tflops = flops / (stage["window_attn_us"] * 1e-6) / 1e12
+    qkv_flops = 3 * 2.0 * w.n_q * w.hidden * w.n_heads * w.head_dim
+    o_flops = 2.0 * w.n_q * w.hidden * w.hidden
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "wan_fused layer-chunk: the wan_window layer-chunk (4680 queries, "
+                        "18720 window keys, 12 heads x 128) with one fused Q/K/V projection "
+                        "(RoPE-K and the K/V append in its epilogue) and V/O at SVD rank 1413 "
+                        "re-densified; the step includes the Q and K projections",
+            "n_q": w.n_q, "n_k": n_k, "rank": rank, "attn_gflop": round(flops / 1e9, 2),
+            "schedule": schedule,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "window_attn_kernel<128> (per-stage pass)",
+        },
+        "stages_us": stage,
+        "stages": {
+            "qkv_TFLOPs": round(qkv_flops / (stage["qkv_proj_rope_k_append_us"] * 1e-6) / 1e12, 1),
+            "o_proj_TFLOPs": round(o_flops / (stage["o_proj_us"] * 1e-6) / 1e12, 1),
+        },
+        "stages_note": "separate untimed pass with events between the stages (each event "
+                       "adds ~2-3 us; stage times include launch gaps)",
+    }
     print(json.dumps(result), flush=True)
 
 

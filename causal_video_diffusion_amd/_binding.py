@@ -21,7 +21,7 @@ STATUS = {0: "UST_OK", 1: "UST_E_NULL", 2: "UST_E_SHAPE", 3: "UST_E_RANGE",
 # every entry point the header declares
 EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
            "ust_window_attn", "ust_window_attn_work_bytes", "ust_window_attn_split",
-           "ust_lowrank_proj", "ust_slot_of_frame", "ust_window_plan",
+           "ust_qkv_append", "ust_lowrank_proj", "ust_slot_of_frame", "ust_window_plan",
            "ust_status_str", "ust_last_error")
 
 
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "ust_window_attn_work_bytes": (SZ, [GP, I32]),
         "ust_window_attn_split": (I32, [GP, KP, P, P, P, I32, I32, I32, F32, P, P, P, SZ,
                                         I32, P]),
+        "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, P, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_slot_of_frame": (I32, [KP, I32]),
         "ust_window_plan": (I32, [GP, KP, I32, I32, IP, IP, I32, IP]),
@@ -159,6 +160,13 @@ def ust_window_attn_split(g: Geom, ring: Kv, q, cos_tab, sin_tab, n_tab_frames: 
                                         frame_start, n_recent, scale, _ptr(out),
                                         _ptr(lse), _ptr(work), nbytes, n_workgroups,
                                         _stream(stream)))
+
+
+def ust_qkv_append(g: Geom, ring: Kv, x, w_qkv, hidden: int, cos_tab, sin_tab,
+                   n_tab_frames: int, frame_start: int, q_out, stream=None) -> None:
+    _check(load().ust_qkv_append(ctypes.byref(g), ctypes.byref(ring), _ptr(x), _ptr(w_qkv),
+                                 hidden, _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
+                                 frame_start, _ptr(q_out), _stream(stream)))
 
 
 def ust_lowrank_proj(x, a, b, bias, t_work, y, M: int, K: int, r: int, N: int,

@@ -187,9 +187,10 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int BM, int BN, int STAGES>
+// QKV: the fused Q/K/V projection epilogue (QkvEpilogue) instead of Y.
+template <int BM, int BN, int STAGES, bool QKV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_nt_dma_kernel(GemmArgs g) {
+gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   constexpr int MB = BM / 64;              // 32-row blocks of X per wave
   constexpr int NB = BN / 64;              // 32-row blocks of W per wave
   constexpr int FR = NB + MB;              // fragments per 16-wide k substep
@@ -330,8 +331,46 @@ gemm_nt_dma_kernel(GemmArgs g) {
     st = stn;
   }
 
+  // which output of the fused projection this tile is (0 Q, 1 K, 2 V) and
+  // its head; K is rotated in fp32 before its one bf16 rounding
+  int which = 0, h = 0;
+  if constexpr (QKV) {
+    const int HD = e.H * BN;
+    which = n0 / HD;
+    h = (n0 - which * HD) / BN;
+    if (which == 1) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int col = wn * 32 * NB + 32 * i + 8 * qq + 4 * half;   // dims col .. col+3
+#pragma unroll
+          for (int j = 0; j < MB; ++j) {
+            const int m = m0 + wm * 32 * MB + 32 * j + l32;
+            if (m < g.M) {
+              const int64_t trow = (int64_t(e.frame_start) * e.T + m) * (BN / 2) + col / 2;
+              const float2 cs = *reinterpret_cast<const float2*>(e.cos_tab + trow);
+              const float2 sn = *reinterpret_cast<const float2*>(e.sin_tab + trow);
+              f32x16& a4 = acc[i][j];
+              const float x0 = a4[4 * qq], x1 = a4[4 * qq + 1];
+              const float x2 = a4[4 * qq + 2], x3 = a4[4 * qq + 3];
+              a4[4 * qq] = x0 * cs.x - x1 * sn.x;
+              a4[4 * qq + 1] = x0 * sn.x + x1 * cs.x;
+              a4[4 * qq + 2] = x2 * cs.y - x3 * sn.y;
+              a4[4 * qq + 3] = x2 * sn.y + x3 * cs.y;
+            }
+          }
+        }
+    }
+  }
+
   // epilogue: bias, bf16, staged through LDS so each row leaves in 16-byte
-  // pieces that cover it contiguously
+  // pieces that cover it contiguously.  V^T leaves by columns instead: its
+  // staging rows have an odd number of dwords, so the column reads (8 tokens
+  // of one dim per 16-byte piece) hit distinct banks.
+  constexpr int ESV = BN + 2;
+  static_assert(BM * ESV <= STAGES * STAGE, "V staging tile fits in the ring");
+  const int es = QKV && which == 2 ? ESV : ES;
   wait_vm_lds<0>();
   barrier();
 #pragma unroll
@@ -349,37 +388,103 @@ gemm_nt_dma_kernel(GemmArgs g) {
       for (int j = 0; j < MB; ++j) {
         const int row = wm * 32 * MB + 32 * j + l32;
         const f32x16& a4 = acc[i][j];
-        uint2 o;
-        o.x = pack_bf16x2(a4[4 * qq] + bv[0], a4[4 * qq + 1] + bv[1]);
-        o.y = pack_bf16x2(a4[4 * qq + 2] + bv[2], a4[4 * qq + 3] + bv[3]);
-        *reinterpret_cast<uint2*>(lds + row * ES + col) = o;
+        const uint32_t lo = pack_bf16x2(a4[4 * qq] + bv[0], a4[4 * qq + 1] + bv[1]);
+        const uint32_t hi = pack_bf16x2(a4[4 * qq + 2] + bv[2], a4[4 * qq + 3] + bv[3]);
+        if (es == ES) {
+          *reinterpret_cast<uint2*>(lds + row * ES + col) = make_uint2(lo, hi);
+        } else {   // 4-byte aligned only
+          *reinterpret_cast<uint32_t*>(lds + row * ESV + col) = lo;
+          *reinterpret_cast<uint32_t*>(lds + row * ESV + col + 2) = hi;
+        }
       }
     }
   __syncthreads();
   constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
+  static_assert(BM * CPR % 256 == 0, "row pieces split evenly over the threads");
+  if constexpr (!QKV) {
 #pragma unroll
-  for (int idx = tid; idx < BM * CPR; idx += 256) {
-    const int rrow = idx / CPR, c = idx % CPR;
-    const int m = m0 + rrow, n = n0 + c * 8;
-    if (m < g.M && n < g.N)
-      *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.N + n) =
-          *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
+    for (int it = 0; it < BM * CPR / 256; ++it) {
+      const int idx = tid + 256 * it;
+      const int rrow = idx / CPR, c = idx % CPR;
+      const int m = m0 + rrow, n = n0 + c * 8;
+      if (m < g.M && n < g.N)
+        *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.N + n) =
+            *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
+    }
+  } else if (which < 2) {
+    // Q rows to q_out, K rows into the ring slot of the token's frame
+#pragma unroll
+    for (int it = 0; it < BM * CPR / 256; ++it) {
+      const int idx = tid + 256 * it;
+      const int rrow = idx / CPR, c = idx % CPR;
+      const int m = m0 + rrow;
+      if (m < g.M) {
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
+        if (which == 0) {
+          *reinterpret_cast<uint4*>(e.q_out + (int64_t(m) * e.H + h) * BN + c * 8) = v;
+        } else {
+          const int fi = m / e.T, t = m - fi * e.T;
+          *reinterpret_cast<uint4*>(
+              e.k_cache + ((int64_t(e.chunk_slot[fi]) * e.H + h) * e.T + t) * BN + c * 8) = v;
+        }
+      }
+    }
+  } else {
+    // V^T: piece (dim d, 8 tokens from m); 8 consecutive lanes take 8
+    // consecutive token groups of one dim, so they store 128 contiguous bytes.
+    // The tokens of a piece share a frame (the tile starts at a multiple of
+    // 8 and T is a multiple of 8).
+    constexpr int TG = BM / 8;   // token groups per tile, a multiple of 8
+    static_assert(TG % 8 == 0 && BN * TG % 256 == 0, "token groups in blocks of 8");
+#pragma unroll
+    for (int it = 0; it < BN * TG / 256; ++it) {
+      const int idx = tid + 256 * it;
+      const int tg = (idx / (8 * BN)) * 8 + idx % 8;
+      const int d = (idx / 8) % BN;
+      const int m = m0 + tg * 8;
+      if (m < g.M) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = lds[(tg * 8 + 2 * k) * ESV + d];
+          const uint32_t hi = lds[(tg * 8 + 2 * k + 1) * ESV + d];
+          w[k] = lo | (hi << 16);
+        }
+        const int fi = m / e.T, t = m - fi * e.T;
+        *reinterpret_cast<uint4*>(
+            e.v_cache + ((int64_t(e.chunk_slot[fi]) * e.H + h) * BN + d) * e.TV + t) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
   }
 }
 
 }  // namespace
+
+hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_t s) {
+  // one head per output tile: the tile's feature width is the head size
+  if (e.D == 128) {
+    dim3 grid(((g.M + 255) / 256) * (g.N / 128));
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, true>), grid, dim3(256), 0, s, g, e);
+  } else {
+    dim3 grid(((g.M + 191) / 192) * (g.N / 64));
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, true>), grid, dim3(256), 0, s, g, e);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s) {
   if (g.K % 64 == 0 && int64_t(g.M) * g.K < (int64_t(1) << 31) &&
       int64_t(g.N) * g.K < (int64_t(1) << 31)) {
     // narrow outputs (the rank-r factor product) get 192 x 64 tiles, wide
     // ones 256 x 128: at 4680 rows either grid is one round on 256 CUs
+    const QkvEpilogue none{};
     if (g.N <= 768) {
       dim3 grid(((g.M + 191) / 192) * ((g.N + 63) / 64));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, false>), grid, dim3(256), 0, s, g, none);
     } else {
       dim3 grid(((g.M + 255) / 256) * ((g.N + 127) / 128));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, false>), grid, dim3(256), 0, s, g, none);
     }
     return hipGetLastError();
   }

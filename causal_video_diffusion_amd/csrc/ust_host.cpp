@@ -354,6 +354,53 @@ ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void
                      out, lse_opt, true, work, work_bytes, n_workgroups, stream);
 }
 
+ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
+                          const void* w_qkv, int32_t hidden, const float* cos_tab,
+                          const float* sin_tab, int32_t n_tab_frames, int32_t frame_start,
+                          void* q_out, hipStream_t stream) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    s = check_kv(kv);
+    if (s != UST_OK) return s;
+    s = check_ring_size(g, kv);
+    if (s != UST_OK) return s;
+    if (!x || !w_qkv || !cos_tab || !sin_tab || !q_out)
+      return fail(UST_E_NULL, "x, w_qkv, table or q_out pointer is NULL");
+    if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
+        !aligned16(q_out))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    if (hidden <= 0) return fail(UST_E_SHAPE, "hidden %d must be positive", hidden);
+    if (hidden % 64 != 0)
+      return fail(UST_E_UNSUPPORTED, "hidden %d: must be a multiple of 64", hidden);
+    const int32_t T = g->grid_h * g->grid_w;
+    if (T % 8 != 0)
+      return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
+    const int32_t M = T * g->chunk_frames;
+    const int32_t N = 3 * g->n_heads * g->head_dim;
+    if (int64_t(M) * hidden >= (int64_t(1) << 31) || int64_t(N) * hidden >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
+    ust::QkvEpilogue e{};
+    s = chunk_slots(g, kv, n_tab_frames, frame_start, e.chunk_slot);
+    if (s != UST_OK) return s;
+    e.q_out = static_cast<uint16_t*>(q_out);
+    e.k_cache = static_cast<uint16_t*>(kv->k);
+    e.v_cache = static_cast<uint16_t*>(kv->v);
+    e.cos_tab = cos_tab;
+    e.sin_tab = sin_tab;
+    e.T = T;
+    e.TV = ust_v_row_len(T);
+    e.H = g->n_heads;
+    e.D = g->head_dim;
+    e.frame_start = frame_start;
+    const ust::GemmArgs ga{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qkv),
+                           nullptr, nullptr, M, N, hidden};
+    return hip_status(ust::launch_qkv_append(ga, e, stream), "qkv_append launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
 ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const void* bias,
                             void* t_work, void* y, int32_t M, int32_t K, int32_t r, int32_t N,
                             hipStream_t stream) {

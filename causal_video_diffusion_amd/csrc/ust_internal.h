@@ -60,7 +60,24 @@ struct GemmArgs {
   int32_t M, N, K;
 };
 
+// Epilogue of the fused Q/K/V projection: output features [0, HD) are Q,
+// [HD, 2HD) K, [2HD, 3HD) V, one head per tile (the tile's feature width is
+// D).  Q goes to q_out [M][H][D]; K is rotated and V transposed into the
+// chunk's ring slots, as ust_kv_append stores them.
+struct QkvEpilogue {
+  uint16_t* q_out;           // [M][H][D]
+  uint16_t* k_cache;         // [slots][H][T][D]
+  uint16_t* v_cache;         // [slots][H][D][TV]
+  const float* cos_tab;      // [F][T][P]
+  const float* sin_tab;
+  int32_t T, TV, H, D;
+  int32_t frame_start;
+  int32_t chunk_slot[8];     // slot of each chunk frame
+};
+
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
+// X [M][K] W [3HD][K]^T with the QKV epilogue; K % 64 == 0, D in {64, 128}
+hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 // workspace bytes of the key-split schedule over n_wg workgroups

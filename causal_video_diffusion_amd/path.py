@@ -122,6 +122,38 @@ def lowrank_apply(p: LowRank, x: torch.Tensor, y: Optional[torch.Tensor] = None,
     return y
 
 
+def densify(a_bits: np.ndarray, b_bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """W_r = A_r B_r re-densified on the GPU (one bf16 rounding of the fp32
+    product), returned output-major [N][K] for ust_qkv_append or a dense
+    ust_lowrank_proj.  a_bits [K][r], b_bits [r][N]; the rank is zero-padded
+    to a multiple of 8, which leaves the product unchanged.  Worth it when r
+    is above the break-even K N / (K + N) (768 at 1536 x 1536)."""
+    K, r = a_bits.shape
+    N = b_bits.shape[1]
+    rp = -(-r // 8) * 8
+    a_pad = np.zeros((K, rp), np.uint16)
+    a_pad[:, :r] = a_bits
+    b_pad = np.zeros((rp, N), np.uint16)
+    b_pad[:r] = b_bits
+    # W_r^T = B_r^T A_r^T: x = B_r^T [N][rp] (B_r output-major), weight rows =
+    # rows of A_r [K][rp] (A_r as stored, input-major)
+    x = to_device_bf16(output_major(b_pad), device)
+    a = to_device_bf16(a_pad, device)
+    y = torch.empty((N, K), dtype=torch.bfloat16, device=device)
+    B.ust_lowrank_proj(x, a, None, None, None, y, N, rp, K, K)
+    return y
+
+
+def qkv_weights(wq_bits: np.ndarray, wk_bits: np.ndarray, wv, device="cuda") -> torch.Tensor:
+    """The fused projection's weight [3 H D][hidden], output-major: W_q, W_k
+    ([in][out] bits) and W_v, given as [in][out] bits or as a device tensor
+    already output-major (e.g. from densify)."""
+    parts = [to_device_bf16(output_major(wq_bits), device),
+             to_device_bf16(output_major(wk_bits), device),
+             wv if isinstance(wv, torch.Tensor) else to_device_bf16(output_major(wv), device)]
+    return torch.cat(parts, dim=0).contiguous()
+
+
 # ------------------------------------------------------------------ layer-chunk
 
 def attn_units(g: B.Geom) -> int:
@@ -201,6 +233,27 @@ def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
                                 bufs.attn_work, 0)
     else:
         B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames,
+                          frame_start, n_recent, scale, bufs.o, bufs.lse)
+    lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
+    return bufs.y
+
+
+def layer_chunk_fused(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
+                      w_qkv: torch.Tensor, wo: LowRank, frame_start: int, n_recent: int,
+                      bufs: LayerBuffers, q_buf: torch.Tensor,
+                      scale: float = 0.0) -> torch.Tensor:
+    """One layer-chunk with the fused projection: Q/K/V in one product whose
+    epilogue rotates K and appends K and V to the ring, then the attention
+    and the output projection.  x: [NQ][hidden]; q_buf: [NQ][H*D]."""
+    hidden = x.shape[1]
+    B.ust_qkv_append(g, ring.abi, x, w_qkv, hidden, table.cos, table.sin, table.n_frames,
+                     frame_start, q_buf)
+    if bufs.attn_work is not None:
+        B.ust_window_attn_split(g, ring.abi, q_buf, table.cos, table.sin, table.n_frames,
+                                frame_start, n_recent, scale, bufs.o, bufs.lse,
+                                bufs.attn_work, 0)
+    else:
+        B.ust_window_attn(g, ring.abi, q_buf, table.cos, table.sin, table.n_frames,
                           frame_start, n_recent, scale, bufs.o, bufs.lse)
     lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
     return bufs.y

@@ -18,6 +18,8 @@
  *                         frames, Table 3)
  *   ust_window_attn_split the same attention with the work divided evenly over
  *                         the workgroups (split key ranges merged afterwards)
+ *   ust_qkv_append        the chunk's Q/K/V projections with the key RoPE and
+ *                         the K/V append fused into the product's epilogue
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
  *
@@ -192,6 +194,31 @@ ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void
                                  int32_t n_recent, float scale, void* out,
                                  float* lse_opt, void* work, size_t work_bytes,
                                  int32_t n_workgroups, hipStream_t stream);
+
+/* The chunk's Q, K and V projections in one pass, with the key RoPE and
+ * the append of ust_kv_append folded into the product's epilogue (abstract:
+ * fused RoPE with cached coefficients, KV cache indexed by frame).  For
+ * every token n of the chunk (frame f = frame_start + n / T) and head h:
+ *   q_out[n][h][:]             = bf16_rne(x[n] W_q^T), un-rotated (the
+ *                                attention rotates the queries itself)
+ *   kv.k[slot(f)][h][n % T][:] = bf16_rne(RoPE(f, y, x) (x[n] W_k^T))
+ *   kv.v[slot(f)][h][:][n % T] = bf16_rne(x[n] W_v^T)
+ * with the rotation applied to the fp32 product before its one rounding.  A
+ * truncated-SVD value projection whose rank r is above the break-even
+ * hidden * H D / (hidden + H D) (768 at 1536 x 1536) enters as its
+ * re-densified W_r = A_r B_r, which ust_lowrank_proj can form (x = B_r
+ * stored output-major, a = A_r stored input-major, b = NULL).
+ *   x:     bf16 [chunk_frames*T][hidden], read.
+ *   w_qkv: bf16 [3 * n_heads * head_dim][hidden], output-major: rows of W_q,
+ *          then of W_k, then of W_v (row j = output feature j).  Read.
+ *   q_out: bf16 [chunk_frames*T][n_heads][head_dim], written.
+ * Arithmetic: bf16 MFMA with fp32 accumulation.
+ * Errors: as ust_kv_append; hidden <= 0 (UST_E_SHAPE), not a multiple of 64
+ * (UST_E_UNSUPPORTED); operands past 32-bit indexing (UST_E_SHAPE). */
+ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
+                          const void* w_qkv, int32_t hidden, const float* cos_tab,
+                          const float* sin_tab, int32_t n_tab_frames, int32_t frame_start,
+                          void* q_out, hipStream_t stream);
 
 /* Low-rank projection Y = (X A_r) B_r (+ bias) (abstract: truncated SVD of
  * the attention value and output projections).

@@ -280,6 +280,29 @@ def test_window_attn_longest_window_short_frames(head_dim, pairs):
                          max_abs=2e-2, rel_l2=1e-3)
 
 
+def test_streaming_far_past_one_clip():
+    """A stream of 40 chunks (frames 0-119) through a 12-slot ring (3 pinned
+    sinks + 9 cycling slots, so the cycling part wraps 13 times) with a RoPE
+    table over all 120 frames: the window keeps the 3 sink frames and the 6
+    most recent ones at any length, and keys keep their absolute positions.
+    Chunks 10, 25 and 39 are compared in full, on both schedules."""
+    w = wl.MID.replace(name="mid_stream", wid=30, n_chunks=40, n_tab_frames=120)
+    for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
+        if c not in (10, 25, 39):
+            continue
+        frames, slots = B.ust_window_plan(g, ring.abi, 3 * c, w.n_recent)
+        assert frames == [0, 1, 2] + list(range(3 * c - 6, 3 * c + 3))
+        assert slots == [0, 1, 2] + [3 + (f - 3) % 9 for f in range(3 * c - 6, 3 * c + 3)]
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
+                                       w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+        for n_wg in (None, 0):
+            print(f"[stream chunk {c} (frames {3 * c}-{3 * c + 2}) n_wg {n_wg}]", flush=True)
+            o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
+            assert_close(_f64(o_gpu), o_ref, f"stream chunk {c} O")
+            assert_close(lse_gpu, lse_ref, f"stream chunk {c} lse", max_abs=2e-2, rel_l2=1e-3)
+
+
 def test_nan_outside_window_and_determinism():
     """Poisoning every slot outside the window (and the value padding) with NaN
     leaves the output bit-identical; two runs agree bit for bit.  Both
@@ -407,6 +430,134 @@ def test_layer_chunk_wan_window_chained():
         y_ref = O.lowrank_proj(o_ref.reshape(len(rows), -1), _f64(ao), _f64(bo))
         print(f"[layer_chunk wan_window chunk {c}]", flush=True)
         assert_close(_f64(P.from_device_bf16(y))[rows], y_ref, f"chunk {c} Y")
+
+
+# ------------------------------------------------------------------ fused Q/K/V projection
+
+def _qkv_case(w, chunks_checked, rows=None, layer=0):
+    """ust_qkv_append on every chunk of w against the oracle: Q = X W_q, and
+    the ring after appending K = X W_k (rotated) and V = X W_v.  Slots no
+    chunk wrote keep the NaN sentinel bit for bit."""
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    wq = wl.dense_weight_bf16(w, wl.TAG_WQ, layer)
+    wk = wl.dense_weight_bf16(w, wl.TAG_WK, layer)
+    wv = wl.dense_weight_bf16(w, wl.TAG_WV, layer)
+    w_qkv = P.qkv_weights(wq, wk, wv)
+    q = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    written = set()
+    for c in range(w.n_chunks):
+        xb = wl.activations(w, c)
+        B.ust_qkv_append(g, ring.abi, P.to_device_bf16(xb), w_qkv, w.hidden, table.cos,
+                         table.sin, w.n_tab_frames, 3 * c, q)
+        torch.cuda.synchronize()
+        X = _f64(xb)
+        k_ref = (X @ _f64(wk)).reshape(w.n_q, w.n_heads, w.head_dim)
+        v_ref = (X @ _f64(wv)).reshape(w.n_q, w.n_heads, w.head_dim)
+        O.kv_append(cache, k_ref, v_ref, cos, sin, 3 * c, 3, w.grid_h, w.grid_w, w.n_slots,
+                    w.n_sink)
+        for i in range(3):
+            written.add(O.slot_of_frame(3 * c + i, w.n_slots, w.n_sink))
+        if c not in chunks_checked:
+            continue
+        print(f"[qkv_append {w.name} chunk {c}]", flush=True)
+        r = np.arange(w.n_q) if rows is None else rows
+        q_ref = X[r] @ _f64(wq)
+        assert_close(_f64(P.from_device_bf16(q))[r], q_ref, f"chunk {c} Q")
+        gk = ring.host_k()
+        gv = ring.host_v_natural()
+        gv_raw = P.from_device_bf16(ring.v)
+        for s_ in range(w.n_slots):
+            if s_ not in written:
+                assert np.all(gk[s_] == NAN_BITS) and np.all(gv_raw[s_] == NAN_BITS), f"slot {s_}"
+                continue
+            tk = (r % w.T) if rows is not None else slice(None)
+            assert_close(_f64(gk[s_])[:, tk], cache.k[s_][:, tk], f"chunk {c} slot {s_} K")
+            assert_close(_f64(gv[s_])[:, tk], cache.v[s_][:, tk], f"chunk {c} slot {s_} V")
+        assert np.all(gv_raw[..., w.T:] == NAN_BITS)   # value row padding untouched
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_wrap", "mid", "mid64"])
+def test_qkv_append_full_compare(name):
+    w = wl.ALL[name]
+    _qkv_case(w, chunks_checked=range(w.n_chunks))
+
+
+def test_qkv_append_wan_window():
+    w = wl.WAN_WINDOW
+    _qkv_case(w, chunks_checked=(0, 5), rows=_sample_rows(w.n_q, 160, seed=3))
+
+
+def test_densified_rank_1413_projection():
+    """The pages' rank, 0.92 x 1536 = 1413, is above the 768 break-even, so the
+    value projection runs dense with W_r = A_r B_r re-densified on the GPU
+    (rank zero-padded to 1416).  W_r, and V = X W_r through the fused
+    projection, against the oracle's fp64 X A_r B_r."""
+    w = wl.WAN_WINDOW
+    a_bits, b_bits = wl.svd_factors_bf16(w, wl.TAG_WV, 1413)
+    wr_t = P.densify(a_bits, b_bits)
+    torch.cuda.synchronize()
+    A, Bm = _f64(a_bits), _f64(b_bits)
+    assert_close(_f64(P.from_device_bf16(wr_t)), (A @ Bm).T, "W_r")
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    wq = wl.dense_weight_bf16(w, wl.TAG_WQ)
+    wk = wl.dense_weight_bf16(w, wl.TAG_WK)
+    w_qkv = P.qkv_weights(wq, wk, wr_t)
+    q = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    xb = wl.activations(w, 0)
+    B.ust_qkv_append(g, ring.abi, P.to_device_bf16(xb), w_qkv, w.hidden, table.cos, table.sin,
+                     w.n_tab_frames, 0, q)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.n_q, 256, seed=4)   # first and last 64 rows, 128 between
+    v_ref = O.lowrank_proj(_f64(xb)[rows], A, Bm).reshape(len(rows), w.n_heads, w.head_dim)
+    gv = ring.host_v_natural()
+    for fi in range(3):
+        sel = rows[(rows >= fi * w.T) & (rows < (fi + 1) * w.T)]
+        assert len(sel) > 0
+        got = _f64(gv[O.slot_of_frame(fi, w.n_slots, w.n_sink)])[:, sel - fi * w.T]
+        ref = v_ref[np.isin(rows, sel)].transpose(1, 0, 2)
+        assert_close(got, ref, f"frame {fi} V = X A_r B_r")
+
+
+def test_layer_chunk_fused_mid():
+    """Fused Q/K/V projection + append, attention, output projection (W_o
+    re-densified from rank 48 factors) over MID's chunks, against the fp64
+    chain X W_q, X W_k, X A_v B_v, attention, (O A_o) B_o."""
+    w = wl.MID
+    g = _g(w)
+    r = 48
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    wq = wl.dense_weight_bf16(w, wl.TAG_WQ)
+    wk = wl.dense_weight_bf16(w, wl.TAG_WK)
+    av, bv = wl.svd_factors_bf16(w, wl.TAG_WV, r)
+    ao, bo = wl.svd_factors_bf16(w, wl.TAG_WO, r)
+    w_qkv = P.qkv_weights(wq, wk, P.densify(av, bv))
+    wo = P.LowRank(P.densify(ao, bo), None)
+    bufs = P.LayerBuffers.alloc(w.n_q, w.hidden, w.n_heads, None, None)
+    q = torch.empty((w.n_q, w.hidden), dtype=torch.bfloat16, device="cuda")
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    for c in range(w.n_chunks):
+        xb = wl.activations(w, c)
+        y = P.layer_chunk_fused(g, ring, table, P.to_device_bf16(xb), w_qkv, wo, 3 * c,
+                                w.n_recent, bufs, q)
+        torch.cuda.synchronize()
+        X = _f64(xb)
+        shape = (w.n_q, w.n_heads, w.head_dim)
+        O.kv_append(cache, (X @ _f64(wk)).reshape(shape),
+                    O.lowrank_proj(X, _f64(av), _f64(bv)).reshape(shape), cos, sin, 3 * c, 3,
+                    w.grid_h, w.grid_w, w.n_slots, w.n_sink)
+        o_ref, _ = O.window_attn(cache, (X @ _f64(wq)).reshape(shape), cos, sin, 3 * c, 3,
+                                 w.grid_h, w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+        y_ref = O.lowrank_proj(o_ref.reshape(w.n_q, -1), _f64(ao), _f64(bo))
+        print(f"[fused layer-chunk mid chunk {c}]", flush=True)
+        assert_close(_f64(P.from_device_bf16(y)), y_ref, f"chunk {c} Y")
 
 
 # ------------------------------------------------------------------ clip schedule

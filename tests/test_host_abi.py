@@ -34,7 +34,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 12
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -202,6 +202,27 @@ def test_window_attn_split_rejects_bad_arguments(lib):
     st, msg = _raw(lib, "ust_window_attn_split", *args, fake, need - 1, 256, None)
     assert st == "UST_E_SHAPE" and "needed" in msg
     assert _raw(lib, "ust_window_attn_split", *args, fake, need, 1 << 17, None)[0] == "UST_E_SHAPE"
+
+
+def test_qkv_append_rejects_bad_arguments(lib):
+    """The fused projection validates like ust_kv_append, then hidden; every
+    call here fails before a launch."""
+    w = wl.WAN_WINDOW
+    g = _geom(w)
+    fake = 0x10000
+    ring = B.Kv(fake, fake, 21, 3)
+    gp, rp = ctypes.byref(g), ctypes.byref(ring)
+    call = lambda x, wq, hidden, n_tab, f0, q: _raw(lib, "ust_qkv_append", gp, rp, x, wq, hidden,
+                                                     fake, fake, n_tab, f0, q, None)
+    assert call(None, fake, 1536, 21, 0, fake)[0] == "UST_E_NULL"
+    assert call(fake, fake, 1536, 21, 0, None)[0] == "UST_E_NULL"
+    assert call(fake + 8, fake, 1536, 21, 0, fake)[0] == "UST_E_ALIGN"
+    assert call(fake, fake, 0, 21, 0, fake)[0] == "UST_E_SHAPE"
+    assert call(fake, fake, 1560, 21, 0, fake)[0] == "UST_E_UNSUPPORTED"   # 1560 % 64 = 24
+    assert call(fake, fake, 1536, 21, 19, fake)[0] == "UST_E_RANGE"     # frames 19..21
+    small = B.Kv(fake, fake, 4, 3)
+    assert _raw(lib, "ust_qkv_append", gp, ctypes.byref(small), fake, fake, 1536, fake, fake,
+                21, 6, fake, None)[0] == "UST_E_RANGE"
 
 
 def test_window_attn_work_bytes(lib):
