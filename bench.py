@@ -2,8 +2,8 @@
 """Benchmark of the windowed chunk-attention hot path on one MI355X.
 
 A step is one layer-chunk of the path at the Wan2.1-1.3B windowed workload,
-steady state (chunk 5: frames 15-17; window = 3 sink + 6 recent + 3 current
-frames = 18720 keys; 4680 queries; 12 heads x 128; rank-512 V/O):
+steady state (chunks 3, 4 and 5 in turn; window = 3 sink + 6 recent + 3
+current frames = 18720 keys; 4680 queries; 12 heads x 128; rank-512 V/O):
     V = (X A_v) B_v  ->  RoPE-K + KV append  ->  window plan + RoPE-Q +
     windowed attention  ->  Y = (O A_o) B_o
 with every input resident in HBM when the timed region starts (the ring holds
@@ -102,7 +102,13 @@ def main():
     if args.workload == "wan_fused":
         return main_fused(args)
     w = wl.ALL[args.workload]
-    C = 5                                   # steady-state chunk
+    C = 5                                   # last chunk prepared
+    # Steady-state chunks timed in turn.  The windowed layer's 21-slot ring
+    # keeps frames 0-17 at once, so chunks 3, 4 and 5 (12-frame windows
+    # each) can run in any order; re-appending a chunk rewrites its slots
+    # with the same values.  The 720p ring (15 slots) holds one steady
+    # window at a time: chunk 5.
+    steady = (3, 4, 5) if w.name == "wan_window" else (5,)
     F0 = 3 * C
     g = cvd.geom(*w.geom_tuple())
     stream = torch.cuda.current_stream()
@@ -124,8 +130,9 @@ def main():
         P.layer_chunk(g, ring, table, x, q, k, wv, wo, 3 * c, w.n_recent, bufs)
     torch.cuda.synchronize()
     x, q, k = chunks[C]
-    frames, _ = B.ust_window_plan(g, ring.abi, F0, w.n_recent)
-    n_k = len(frames) * w.T
+    n_ks = {len(B.ust_window_plan(g, ring.abi, 3 * c, w.n_recent)[0]) * w.T for c in steady}
+    assert len(n_ks) == 1, "the timed chunks have windows of one size"
+    n_k = n_ks.pop()
     flops = attn_flops(w.n_q, n_k, w.head_dim, w.n_heads)
     schedule = P.pick_attn_schedule(g) if args.schedule == "auto" else args.schedule
     split = schedule == "split"
@@ -133,27 +140,30 @@ def main():
         nbytes = B.ust_window_attn_work_bytes(g, 0)
         work = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
 
-    def attention():
+    def attention(q, f0):
         if split:
-            B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
+            B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, f0,
                                     w.n_recent, 0.0, bufs.o, None, work, 0)
         else:
-            B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, F0,
+            B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, f0,
                               w.n_recent, 0.0, bufs.o, None)
 
+    # step i runs the layer-chunk of chunk steady[i % len(steady)]
     # ev: None, or 5 events; all=False records only the two around the
     # attention kernel (each event costs ~2-3 µs of step time, so the timed
     # region carries only those; the per-stage split is a separate pass)
-    def step(ev=None, all=False):
+    def step(i, ev=None, all=False):
+        c = steady[i % len(steady)]
+        xc, qc, kc = chunks[c]
         if ev is not None and all:
             ev[0].record(stream)
-        P.lowrank_apply(wv, x, bufs.v, bufs.t_v)
+        P.lowrank_apply(wv, xc, bufs.v, bufs.t_v)
         if ev is not None and all:
             ev[1].record(stream)
-        B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
+        B.ust_kv_append(g, ring.abi, kc, bufs.v, table.cos, table.sin, w.n_tab_frames, 3 * c)
         if ev is not None:
             ev[2].record(stream)
-        attention()
+        attention(qc, 3 * c)
         if ev is not None:
             ev[3].record(stream)
         P.lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
@@ -168,8 +178,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, len(steady))):   # every timed chunk appended once
+        step(i)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -178,7 +188,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step(i, evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -188,7 +198,7 @@ def main():
     # per-stage split, outside the timed region, with all five events
     sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(sevs[i], all=True)
+        step(i, sevs[i], all=True)
     torch.cuda.synchronize()
     names = ["v_proj_us", "rope_k_append_us", "window_attn_us", "o_proj_us"]
     stage = {n: 1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs]))
@@ -231,7 +241,9 @@ def main():
                         f"{w.n_heads} heads x {w.head_dim}, {w.grid_h}x{w.grid_w} = {w.T} "
                         f"tokens/frame, 3-frame chunk = {w.n_q} queries, window {w.n_sink} "
                         f"sink + {w.n_recent} recent + 3 current frames = {n_k} keys, "
-                        f"{w.n_slots}-slot ring, rank-{w.rank} V/O, steady-state chunk {C}",
+                        f"{w.n_slots}-slot ring, rank-{w.rank} V/O, steady-state chunk"
+                        + (f"s {', '.join(map(str, steady))} in turn" if len(steady) > 1
+                           else f" {steady[0]}"),
             "n_q": w.n_q, "n_k": n_k, "n_heads": w.n_heads, "head_dim": w.head_dim,
             "rank": w.rank, "attn_gflop": round(flops / 1e9, 2),
             "schedule": schedule,
