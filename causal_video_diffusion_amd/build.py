@@ -70,7 +70,28 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libust.so failed:\n{r.stderr}")
     os.replace(tmp, OUT)
+    _build_c_check(verbose)
     return OUT
+
+
+C_CHECK = os.path.join(OBJ, "c_abi_check")
+
+
+def _build_c_check(verbose: bool) -> None:
+    """tests/c_abi_check.c: a C11 program that uses libust.so through its C
+    ABI alone (run on the GPU by the parity tests).  Built here, on the build
+    host, so that no test compiles anything."""
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), src, "-o", C_CHECK, "-L", PKG, "-lust",
+           "-Wl,-rpath,$ORIGIN/..", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling c_abi_check failed:\n{r.stderr}")
 
 
 if __name__ == "__main__":

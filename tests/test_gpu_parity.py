@@ -432,6 +432,22 @@ def test_layer_chunk_wan_window_chained():
         assert_close(_f64(P.from_device_bf16(y))[rows], y_ref, f"chunk {c} Y")
 
 
+# ------------------------------------------------------------------ the C ABI from C
+
+def test_c_program_drives_the_library():
+    """tests/c_abi_check.c (built with the library): plain C11 through
+    include/ust.h alone, on the GPU -- error statuses, V = 1 gives 1, split
+    and unsplit schedules agree."""
+    import os
+    import subprocess
+    from causal_video_diffusion_amd import build
+    assert os.path.exists(build.C_CHECK), "c_abi_check is built with libust.so by build()"
+    print("[c_abi_check]", flush=True)
+    r = subprocess.run([build.C_CHECK], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
 # ------------------------------------------------------------------ fused Q/K/V projection
 
 def _qkv_case(w, chunks_checked, rows=None, layer=0):
