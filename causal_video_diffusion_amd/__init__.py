@@ -9,4 +9,6 @@ HIP kernels.  `_binding` exposes the C entry points under the same names;
 """
 from ._binding import (UstError, Geom, Kv, geom, kv, load, ust_v_row_len,  # noqa: F401
                        ust_rope_table_build, ust_kv_append, ust_window_attn,
-                       ust_lowrank_proj, ust_slot_of_frame, ust_window_plan)
+                       ust_lowrank_proj, ust_slot_of_frame, ust_window_plan,
+                       ust_window_attn_split, ust_window_attn_work_bytes,
+                       ust_qkv_append)
