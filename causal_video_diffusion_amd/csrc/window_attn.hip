@@ -21,9 +21,13 @@
 //    l and l^32.  The query rotation, the softmax scale and log2(e) are
 //    folded into the bf16 query fragments once per workgroup.
 //  * The score accumulators start at -m (the lane's running reference max),
-//    so the MFMA yields s - m directly.  The reference only moves when a
-//    tile's scores exceed it by more than 2^8 (and on the first tile), so the
-//    O/l rescale is skipped on almost every tile; the final normalisation by
+//    so the MFMA yields s - m directly.  The reference is set from the exact
+//    tile max on a segment's first tile; after that the tile max is not
+//    taken at all unless the running sum leaves [0, 2^64] (a probability
+//    large enough to risk overflow, an infinity or a NaN): then the raw
+//    scores, still in registers, set a new reference (if they exceed the old
+//    one by more than 2^8) and the tile is redone.  So almost every tile
+//    costs its exponentials, sums and packs only; the final normalisation by
 //    the running sum makes the result exact regardless of the reference.
 //  * The A-operand rows of S^T are permuted (bits 2 and 3 of the key index
 //    swapped) so that each lane's 8 score registers of one 16-key group hold
@@ -63,6 +67,7 @@ constexpr int kStages = 4;     // LDS ring of K/V tiles
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr float kRescale = 8.0f;  // move the reference max when exceeded (log2 units)
+constexpr float kSumBound = 0x1p64f;  // a lane's running sum above this triggers a rescale
 
 // swap bits 2 and 3 of a row index within a 32-row MFMA block
 __device__ __forceinline__ int perm_row(int i) {
@@ -381,20 +386,22 @@ window_attn_kernel(AttnArgs a) {
             if (key >= nk) sacc[kb][r] = -INFINITY;
           }
       }
-      // tile max: a tree of independent max3 ops, not one long dependent chain
-      float m4[4];
+      // The exact tile max (shared by lanes l and l^32) is taken on the
+      // segment's first tile, where it sets the reference, and otherwise only
+      // when the tile's sum leaves [0, kSumBound]: a probability so large it
+      // could overflow, an infinity or a NaN.  The scores are kept until that
+      // test, so the rare path rescales and redoes the tile.
+      auto rescale = [&](bool first) __attribute__((always_inline)) {
+        float m4[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kb = c >> 1, r0 = 8 * (c & 1);
-        m4[c] = fmaxf(fmaxf(fmaxf(sacc[kb][r0], sacc[kb][r0 + 1]), sacc[kb][r0 + 2]),
-                      fmaxf(fmaxf(sacc[kb][r0 + 3], sacc[kb][r0 + 4]),
-                            fmaxf(fmaxf(sacc[kb][r0 + 5], sacc[kb][r0 + 6]), sacc[kb][r0 + 7])));
-      }
-      float tmax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-      tmax = pair_max(tmax);
-      const bool need = (j == 0) || (tmax > kRescale);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float shift = need ? tmax : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          const int kb = c >> 1, r0 = 8 * (c & 1);
+          m4[c] = fmaxf(fmaxf(fmaxf(sacc[kb][r0], sacc[kb][r0 + 1]), sacc[kb][r0 + 2]),
+                        fmaxf(fmaxf(sacc[kb][r0 + 3], sacc[kb][r0 + 4]),
+                              fmaxf(fmaxf(sacc[kb][r0 + 5], sacc[kb][r0 + 6]), sacc[kb][r0 + 7])));
+        }
+        const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        const float shift = (first || tmax > kRescale) ? tmax : 0.f;
         const float alpha = __builtin_amdgcn_exp2f(-shift);
         mref += shift;
         lrow *= alpha;
@@ -406,30 +413,43 @@ window_attn_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
+      };
+      // probabilities (32 independent exp2) straight into bf16 pairs, the row
+      // sum in fp32 in four independent partial sums (plain adds:
+      // dot-product instructions would contend with the partner wave's MFMAs)
+      auto probs = [&]() __attribute__((always_inline)) -> float {
+        float ls[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * g + 2 * e;
+              const float p0 = __builtin_amdgcn_exp2f(sacc[kb][r]);
+              const float p1 = __builtin_amdgcn_exp2f(sacc[kb][r + 1]);
+              const int c = (kb * 16 + r) & 3;   // 0 or 2
+              if (kb == 0 && g == 0 && e < 2) {
+                ls[c] = p0;
+                ls[c + 1] = p1;
+              } else {
+                ls[c] += p0;
+                ls[c + 1] += p1;
+              }
+              pk[e] = pack_bf16x2(p0, p1);
+            }
+            pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+          }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      if (j == 0) rescale(true);
+      float lnew = lrow + probs();
+      if (__builtin_amdgcn_ballot_w64(!(lnew <= kSumBound))) {
+        rescale(false);
+        lnew = lrow + probs();
       }
-      // probabilities in place (32 independent exp2), the row sum in fp32 in
-      // four independent partial sums (plain adds: dot-product instructions
-      // would contend with the partner wave's MFMAs), then bf16 pairs
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ls[r & 3] += sacc[kb][r];
-      lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pk[e] = pack_bf16x2(sacc[kb][8 * g + 2 * e], sacc[kb][8 * g + 2 * e + 1]);
-          pf[kb][g] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        }
+      lrow = lnew;
     };
 
     // ---- the phase schedule ----

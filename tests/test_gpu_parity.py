@@ -331,6 +331,65 @@ def test_nan_outside_window_and_determinism():
             break
 
 
+def test_window_attn_scores_far_above_the_first_tile():
+    """Keys of chunks 0, 1, 2, 3 scaled by 1, 4, 16, 64 (powers of two: exact
+    in bf16), so that along the window later tiles score far above the
+    reference max set on the first one: by up to ~2^4 (large probabilities,
+    no rescale), ~2^6 (a running sum past 2^64: rescale with finite values)
+    and ~2^8 (exp2 overflows to infinity: rescale from the raw scores).
+    Both schedules, so segments also start inside the scaled chunks.
+
+    Scores this large are only as exact as the bf16 query fragments (each
+    rotated, scaled query element is rounded to bf16: relative error at most
+    2^-8, bf16 having 8 significant bits), so the checks are ones that
+    rounding cannot disturb:
+    - every window value row of a head is the same row v, so O = v whatever
+      the weights: the kernel's sum bf16(p) v / sum p (fp32) is within
+      2^-8 |v| of v, less than one bf16 ulp of v, so the bf16 output is
+      within one ulp of v (and finite: no infinity or NaN from an overflowed
+      tile leaks through);
+    - the log-sum-exp, which counts every tile's mass against its reference,
+      moves with the scores by at most the largest score error,
+      2^-8 sum_d |q_d k_d| scale (1% added for the fp32 rotation and
+      accumulation): that bound, per query row."""
+    w = wl.MID
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    vrow = wl.chunk_tokens(w, wl.TAG_V, 0)[:1]                 # [1][H][D]
+    vb = np.repeat(vrow, w.n_q, axis=0)
+    v = _f64(vrow)[0]                                          # [H][D]
+    for c, e in enumerate((0, 2, 4, 6)):
+        kb = wl.f32_to_bf16_bits((_f64(wl.chunk_tokens(w, wl.TAG_K, c)) * 2.0 ** e).astype(np.float32))
+        B.ust_kv_append(g, ring.abi, P.to_device_bf16(kb), P.to_device_bf16(vb),
+                        table.cos, table.sin, w.n_tab_frames, 3 * c)
+        O.kv_append(cache, _f64(kb), _f64(vb), cos, sin, 3 * c, 3, w.grid_h,
+                    w.grid_w, w.n_slots, w.n_sink)
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
+                                       w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+        f, y, x = O.chunk_positions(3 * c, 3, w.grid_h, w.grid_w)
+        qr = np.abs(O.rope_apply(_f64(qb), cos[f, y, x][:, None, :], sin[f, y, x][:, None, :]))
+        _, slots = O.window_slots(3 * c, 3, w.n_sink, w.n_recent, w.n_slots)
+        bound = np.empty((w.n_heads, w.n_q))
+        for h in range(w.n_heads):
+            kabs = np.abs(cache.k[slots][:, h].reshape(-1, w.head_dim))
+            bound[h] = 1.01 * 2.0 ** -8 * scale * (qr[:, h] @ kabs.T).max(axis=1)
+        for n_wg in (None, 5, 37):
+            print(f"[scaled keys chunk {c} (x{2 ** e}) n_wg {n_wg}]", flush=True)
+            o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
+            o = _f64(o_gpu)
+            assert_close(o, o_ref, f"scaled chunk {c} O")
+            assert np.all(np.abs(o - v) <= _bf16_ulp(v)), f"chunk {c}: O more than one ulp from v"
+            err = np.abs(lse_gpu - lse_ref)
+            print(f"  lse: max err {err.max():.3e}, max err / bound {(err / bound).max():.3f}",
+                  flush=True)
+            assert np.all(err <= bound + 1e-4 * (1 + np.abs(lse_ref))), f"chunk {c} lse"
+
+
 def test_v_one_gives_one_and_k_zero_gives_mean():
     w = wl.MID
     g = _g(w)
