@@ -7,8 +7,9 @@
 //  * One workgroup of 8 waves per CU owns 256 queries of one head (32 per
 //    wave), so every K/V tile brought into LDS feeds 256 queries.  Waves w
 //    and w+4 share a SIMD.  The two groups (waves 0-3, 4-7) run a phase
-//    apart ("ping-pong"): in every phase one group issues MFMAs (PV of the
-//    previous tile, then QK of the current one) while the other computes the
+//    apart ("ping-pong"): in every phase one group issues MFMAs (QK of the
+//    current tile, then PV of the previous one, as one pipeline of LDS
+//    fragment reads running ahead of the MFMAs) while the other computes the
 //    softmax of its current tile, so on each SIMD one wave's VALU work runs
 //    under the other wave's matrix work.  A workgroup barrier separates the
 //    phases.
@@ -372,6 +373,30 @@ window_attn_kernel(AttnArgs a) {
       sched_pipeline<4 * DB>();
     };
 
+    // ---- both products in one read/MFMA pipeline, so the first value
+    // fragments are read while the last score MFMAs run ----
+    auto qkpv = [&](auto kbuf, auto vbuf) __attribute__((always_inline)) {
+      const uint16_t* K = kstage(kbuf);
+      const uint16_t* V = vstage(vbuf);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = -mref;
+      bf16x8 kf[2 * KS], vf[4 * DB];
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i)
+        kf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(K + koffr[i >> 1] + (i & 1) * 32 * D));
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i)
+        vf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(V + voffr[i / DB] + (i % DB) * 32 * kBN));
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i)
+        oacc[i % DB] = mfma32(vf[i], pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
+      sched_pipeline<2 * KS + 4 * DB>();
+    };
+
     // ---- online softmax of the segment's j-th tile (key tile t = k0 + j):
     // bf16 probabilities into pf ----
     auto softmax = [&](int j) __attribute__((always_inline)) {
@@ -456,7 +481,7 @@ window_attn_kernel(AttnArgs a) {
     // Tiles are counted from the segment's first (j = 0 is key tile k0).
     // Every wave runs the same sequence; group B starts one barrier later, so
     // its phases are offset by one from group A's:
-    //   MFMA phase j:    QK(j); PV(j-1); barrier
+    //   MFMA phase j:    QK(j) and PV(j-1) in one pipeline; barrier
     //   softmax phase j: request own share of tile j+L; softmax(j); wait for own
     //                    share of tile j+L-1; barrier
     // with L = 2 for group A and L = 3 for group B, so every share of tile v is
@@ -469,10 +494,15 @@ window_attn_kernel(AttnArgs a) {
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     const int lead = group_a ? 2 : 3;
-    auto step = [&](int j, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
+    // MODE 0: the first tile (QK only); 1: QK(j) and PV(j-1); 2: the last PV
+    auto step = [&](auto mode, int j, auto cur, auto prev, auto st2, auto st3) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode)::value;
       __builtin_amdgcn_s_setprio(2);
-      if (j < nseg && wave_busy) qk(cur);   // first, so its scores are ready for softmax(j)
-      if (j >= 1 && wave_busy) pv(prev);
+      if (wave_busy) {   // QK first, so its scores are ready for softmax(j)
+        if constexpr (MODE == 1) qkpv(cur, prev);
+        else if constexpr (MODE == 0) qk(cur);
+        else pv(prev);
+      }
       __builtin_amdgcn_s_setprio(0);
       barrier();
       const int v = j + lead;      // tile this wave requests now
@@ -480,7 +510,7 @@ window_attn_kernel(AttnArgs a) {
         if (group_a) issue(k0 + v, st2);
         else issue(k0 + v, st3);
       }
-      if (j < nseg && wave_busy) softmax(j);
+      if (MODE != 2 && wave_busy) softmax(j);
       if (v < nseg) wait_vmcnt<NLD>();   // own share of tile v-1 landed
       else wait_vmcnt<0>();
       barrier();
@@ -492,11 +522,23 @@ window_attn_kernel(AttnArgs a) {
     wait_vmcnt<0>();
     barrier();                        // tiles 0 .. lead-1 are in LDS
     if (!group_a) barrier();          // group B runs one phase behind
-    for (int j = 0; j <= nseg; j += 4) {
-      step(j, S0{}, S3{}, S2{}, S3{});
-      if (j + 1 <= nseg) step(j + 1, S1{}, S0{}, S3{}, S0{});
-      if (j + 2 <= nseg) step(j + 2, S2{}, S1{}, S0{}, S1{});
-      if (j + 3 <= nseg) step(j + 3, S3{}, S2{}, S1{}, S2{});
+    // The first tile and the last PV are peeled off, so that the unrolled
+    // loop holds one kind of MFMA phase and keeps its accumulators in place.
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
+    step(M0{}, 0, S0{}, S3{}, S2{}, S3{});
+    for (int j = 1; j < nseg; j += 4) {
+      step(M1{}, j, S1{}, S0{}, S3{}, S0{});
+      if (j + 1 < nseg) step(M1{}, j + 1, S2{}, S1{}, S0{}, S1{});
+      if (j + 2 < nseg) step(M1{}, j + 2, S3{}, S2{}, S1{}, S2{});
+      if (j + 3 < nseg) step(M1{}, j + 3, S0{}, S3{}, S2{}, S3{});
+    }
+    switch ((nseg - 1) & 3) {   // PV of the last tile, from its stage
+      case 0: step(M2{}, nseg, S0{}, S0{}, S0{}, S0{}); break;
+      case 1: step(M2{}, nseg, S0{}, S1{}, S0{}, S0{}); break;
+      case 2: step(M2{}, nseg, S0{}, S2{}, S0{}, S0{}); break;
+      default: step(M2{}, nseg, S0{}, S3{}, S0{}, S0{}); break;
     }
     if (group_a) barrier();           // match group B's extra barrier
 
