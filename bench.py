@@ -45,8 +45,8 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # whenever the attention kernels change (absent = not measured for the
 # current kernels).
 ATTN_TRAFFIC_BYTES = {
-    ("wan_window", "whole"): (2 * 108073 + 14042) * 1024,
-    ("wan_720p", "split"): (2 * (593425 + 17007) + 58523 + 204) * 1024,   # attention + merge
+    ("wan_window", "whole"): (2 * 109091 + 17699) * 1024,
+    ("wan_720p", "split"): (2 * (590041 + 17004) + 62659 + 204) * 1024,   # attention + merge
 }
 
 
