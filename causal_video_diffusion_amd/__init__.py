@@ -1,7 +1,7 @@
 """MI355X-native (gfx950) windowed chunk attention for causal video diffusion.
 
 The per-chunk DiT self-attention path of UnStep (arXiv 2609.32518): 3-D RoPE
-from cached coefficients, KV append into a frame-slot ring, chunk-causal
+from a precomputed cos/sin table, KV append into a frame-slot ring, chunk-causal
 attention over a limited temporal window, and truncated-SVD value/output
 projections, as the C-ABI library libust.so (include/ust.h) over hand-written
 HIP kernels.  `_binding` exposes the C entry points under the same names;

@@ -1,7 +1,7 @@
 // Chunk-causal attention over the limited temporal window (UnStep, abstract:
-// "limiting the temporal window retained in the attention KV cache"; chunks
-// of three latent frames, Table 3), with the query RoPE fused into the Q-tile
-// load (abstract: fused RoPE with cached coefficients).
+// the attention KV cache keeps only a limited window of latent frames; Table
+// 3: chunks of three latent frames), with the query RoPE fused into the
+// Q-tile load (abstract: RoPE applied from precomputed coefficients).
 //
 // Design (gfx950, wave64, bf16 MFMA 32x32x16 with fp32 accumulation):
 //  * One workgroup of 8 waves per CU owns 256 queries of one head (32 per

@@ -6,16 +6,16 @@
  * Steps Than Distillation"), as a C ABI over hand-written gfx950 kernels:
  *
  *   ust_rope_table_build  cos/sin coefficients of the 3-D RoPE, cached once
- *                         (abstract: fused RoPE "with cached coefficients")
+ *                         (abstract: RoPE from precomputed coefficients)
  *   ust_kv_append         RoPE the chunk's keys and store keys and values in
- *                         the frame slots of a KV ring (abstract: KV cache,
- *                         "KV indexing")
+ *                         the frame slots of a KV ring (abstract: the KV
+ *                         cache and its indexing)
  *   ust_window_attn       RoPE the chunk's queries and attend over the limited
  *                         temporal window: sink frames, recent frames, and
  *                         the chunk itself, bidirectional inside the window
- *                         (abstract: "limiting the temporal window retained in
- *                         the attention KV cache"; chunks of three latent
- *                         frames, Table 3)
+ *                         (abstract: the attention KV cache keeps a limited
+ *                         window of latent frames; Table 3: chunks of three
+ *                         latent frames)
  *   ust_window_attn_split the same attention with the work divided evenly over
  *                         the workgroups (split key ranges merged afterwards)
  *   ust_qkv_append        the chunk's Q/K/V projections with the key RoPE and
@@ -113,7 +113,7 @@ int32_t ust_v_row_len(int32_t tokens_per_frame);
 ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double theta,
                                 float* cos_out, float* sin_out, hipStream_t stream);
 
-/* Append one chunk to the KV ring (abstract: KV cache and KV indexing).
+/* Append one chunk to the KV ring (abstract: the KV cache and its indexing).
  * For every token n of the chunk (frame f = frame_start + n / T at (y, x))
  * and head h:
  *   kv.k[slot(f)][h][n % T][:]  = bf16_rne(RoPE(f, y, x) k_new[n][h][:])
@@ -197,7 +197,7 @@ ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void
 
 /* The chunk's Q, K and V projections in one pass, with the key RoPE and
  * the append of ust_kv_append folded into the product's epilogue (abstract:
- * fused RoPE with cached coefficients, KV cache indexed by frame).  For
+ * RoPE from precomputed coefficients, KV cache indexed by frame).  For
  * every token n of the chunk (frame f = frame_start + n / T) and head h:
  *   q_out[n][h][:]             = bf16_rne(x[n] W_q^T), un-rotated (the
  *                                attention rotates the queries itself)

@@ -17,7 +17,7 @@ def rope_rotate(vec: Sequence[float], f: int, y: int, x: int,
     """RoPE of one head vector as complex multiplication: the pair
     (v[2p], v[2p+1]) is the complex number v[2p] + i v[2p+1], multiplied by
     exp(i * pos * theta**(-j/n)) for pair j of its axis (UnStep, abstract:
-    3-D RoPE with cached coefficients; axis split is a reading)."""
+    3-D RoPE from precomputed coefficients; axis split is a reading)."""
     out = []
     p = 0
     for axis_pairs, pos in zip(pairs, (f, y, x)):

@@ -34,7 +34,8 @@ __all__ = [
 
 
 # ------------------------------------------------------------------ 3-D RoPE
-# UnStep, abstract: the runtime stack applies RoPE "with cached coefficients".
+# UnStep, abstract: the runtime stack applies RoPE from precomputed cos/sin
+# coefficients.
 # READING: the head dimension is split into P = D/2 rotation pairs; the first
 # pairs_t pairs rotate with the latent-frame index, the next pairs_h with the
 # token row, the last pairs_w with the token column (the 3-D RoPE of the
@@ -103,8 +104,8 @@ def chunk_positions(frame_start: int, chunk_frames: int, grid_h: int,
 
 
 # ------------------------------------------------------------------ KV cache
-# UnStep, abstract: the KV cache keeps a limited temporal window; the runtime
-# stack has "more efficient ... KV indexing".
+# UnStep, abstract: the KV cache keeps a limited temporal window, and the
+# runtime stack speeds up how the cache is indexed.
 # READING: the cache holds one slot per latent frame.  The first n_sink frames
 # (attention sinks, pinned) keep slots 0..n_sink-1; every later frame goes to
 # a ring over the remaining n_slots - n_sink slots.
