@@ -21,6 +21,10 @@ restate its formula; see tests/test_oracle_pins.py):
   lowrank_proj                pinned (full rank = dense, Eckart-Young on the
                               factors, associativity, brute force)
   clip_schedule               pinned (forward counts printed in Table 3)
-  shift_sigma                 pinned (values printed in Table 4)
+  shifted_sigma, dit_label    pinned (levels and labels printed in Table 4)
+  flow_step, sample_chunk     pinned (forward counts printed in Table 3, the
+                              level endpoints of Table 4, recovery of the
+                              clean latent from exact velocities, scalar
+                              brute force by another algebraic route)
 """
 from .ust_oracle import *  # noqa: F401,F403

@@ -109,3 +109,35 @@ def matmul(a, b):
     n, k, m = len(a), len(b), len(b[0])
     return [[sum(a[i][t] * b[t][j] for t in range(k)) for j in range(m)]
             for i in range(n)]
+
+
+def shifted_sigma(raw: int, shift: float = 5.0, n_train: int = 1000) -> float:
+    """Table 4's shift mapping written as 1 / ((1/u - 1) / shift + 1)."""
+    u = raw / n_train
+    if u == 0:
+        return 0.0
+    return 1.0 / ((1.0 / u - 1.0) / shift + 1.0)
+
+
+def sample_chunk(dit, x_init: Sequence[float], noises, raw_steps: Sequence[int],
+                 sigma_star: float, shift: float = 5.0):
+    """The sampler of one chunk with scalar loops (UnStep, Tables 3 and 4;
+    readings as in ust_oracle): renoising written as x0 + s (eps - x0).
+    Returns (chunk kept, levels, labels)."""
+    levels = [shifted_sigma(r, shift) for r in raw_steps] + [float(sigma_star)]
+    x = [float(a) for a in x_init]
+    seen, labels = [], []
+    for i in range(len(raw_steps)):
+        s, s_next = levels[i], levels[i + 1]
+        v = dit(x, 1000.0 * s)
+        seen.append(s)
+        labels.append(1000.0 * s)
+        est = [x[k] - s * v[k] for k in range(len(x))]
+        if s_next == 0:
+            x = est
+        else:
+            x = [est[k] + s_next * (noises[i][k] - est[k]) for k in range(len(x))]
+    v = dit(x, 0.0)
+    seen.append(levels[-1])
+    labels.append(0.0)
+    return [x[k] - levels[-1] * v[k] for k in range(len(x))], seen, labels

@@ -29,7 +29,8 @@ __all__ = [
     "pair_axis", "rope_frequencies", "rope_table", "rope_apply",
     "chunk_positions", "slot_of_frame", "window_frames", "window_slots",
     "KVCache", "kv_append", "window_attn", "lowrank_proj", "clip_schedule",
-    "rne_bf16",
+    "RAW_STEPS_4", "RAW_STEPS_2", "shifted_sigma", "dit_label", "flow_step",
+    "sample_chunk", "rne_bf16",
 ]
 
 
@@ -263,6 +264,86 @@ def clip_schedule(n_chunks: int, first_steps: int, later_steps: int,
         if clean_pass:
             out.append((c, steps, True))
     return out
+
+
+# ------------------------------------------------------------------ sampler
+# UnStep, Table 4: the few-step model's four denoising levels are the raw
+# timesteps 1000, 750, 500, 250 after a shift-5 mapping, giving noise levels
+# sigma = 1, 15/16, 5/6, 5/8 and DiT labels t = 1000 sigma; the clean-cache
+# forward runs at label 0, on the clean chunk (Self Forcing: sigma 0) or on
+# the chunk renoised to sigma* = 0.02 (UnStep).  Abstract: UnStep renoises the
+# generated frames to a nearly clean level and lets the clean-cache forward,
+# which runs anyway, refine them.  Table 3: four denoising forwards for the
+# first chunk, two for each later one, plus the clean-cache forward.
+# READING (flow matching, this model family's parameterisation; the term is
+# on the pages' glossary): a latent at level sigma is
+# x = (1 - sigma) x0 + sigma eps, the DiT predicts the velocity
+# v = eps - x0, so the denoised estimate is x0_hat = x - sigma v.
+# READING: between denoising steps the estimate is renoised to the next level
+# with a fresh draw, x' = (1 - sigma') x0_hat + sigma' eps'; after the last
+# step, to sigma* for the clean-cache forward.
+# READING: the later chunks' two steps are the raw timesteps 1000 and 500
+# (every other one of the four); the pages do not say which two.
+# READING: the chunk UnStep keeps is the clean-cache forward's estimate at the
+# true level, x_in - sigma* v*; with sigma* = 0 (Self Forcing) that is the
+# clean chunk itself, unchanged.
+
+RAW_STEPS_4 = (1000, 750, 500, 250)
+RAW_STEPS_2 = (1000, 500)
+
+
+def shifted_sigma(raw, shift: float = 5.0, n_train: int = 1000) -> np.ndarray:
+    """Noise level of raw timestep(s) after the shift mapping:
+    sigma = shift u / (1 + (shift - 1) u), u = raw / n_train (Table 4)."""
+    u = np.asarray(raw, dtype=np.float64) / n_train
+    return shift * u / (1.0 + (shift - 1.0) * u)
+
+
+def dit_label(sigma, n_train: int = 1000) -> np.ndarray:
+    """The timestep label the DiT receives at level sigma (Table 4)."""
+    return n_train * np.asarray(sigma, dtype=np.float64)
+
+
+def flow_step(x: np.ndarray, v: np.ndarray, noise: Optional[np.ndarray],
+              sigma: float, sigma_next: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One sampler step at level sigma: the denoised estimate
+    x0_hat = x - sigma v, and the latent renoised to sigma_next,
+    (1 - sigma_next) x0_hat + sigma_next noise (noise unused at
+    sigma_next = 0).  Returns (x0_hat, x_next), fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    x0 = x - float(sigma) * v
+    if sigma_next == 0:
+        return x0, x0.copy()
+    nz = np.asarray(noise, dtype=np.float64)
+    return x0, (1.0 - float(sigma_next)) * x0 + float(sigma_next) * nz
+
+
+def sample_chunk(dit, x_init: np.ndarray, noises: Sequence[np.ndarray],
+                 raw_steps: Sequence[int], sigma_star: float,
+                 shift: float = 5.0) -> Tuple[np.ndarray, List[float], List[float]]:
+    """One chunk of the sampler: a denoising forward per raw step, then the
+    clean-cache forward.  dit(x, t) returns the DiT's velocity for latent x
+    at label t.  x_init is the chunk's initial noise (level sigma_0 = 1 at raw
+    1000); noises[i] is the draw used to renoise after denoising step i (the
+    last one renoises to sigma_star; unused when sigma_star = 0).
+    Returns (the chunk kept, the levels the latent was at for each forward,
+    the labels passed), so len(levels) is the chunk's forward count."""
+    sig = [float(s) for s in shifted_sigma(raw_steps, shift)]
+    x = np.asarray(x_init, dtype=np.float64)
+    levels, labels = [], []
+    for i, s in enumerate(sig):
+        nxt = sig[i + 1] if i + 1 < len(sig) else float(sigma_star)
+        v = dit(x, float(dit_label(s)))
+        levels.append(s)
+        labels.append(float(dit_label(s)))
+        _, x = flow_step(x, v, noises[i] if nxt != 0 else None, s, nxt)
+    # the clean-cache forward: label 0, latent at sigma_star
+    v = dit(x, 0.0)
+    levels.append(float(sigma_star))
+    labels.append(0.0)
+    x0, _ = flow_step(x, v, None, float(sigma_star), 0.0)
+    return x0, levels, labels
 
 
 # ------------------------------------------------------------------ rounding

@@ -455,3 +455,105 @@ def test_clip_schedule_forward_counts():
             assert fw[-1][2] and not any(s[2] for s in fw[:-1])
         n += 1
     assert n == 2
+
+
+# ---------------------------------------------------------------- sampler
+
+def test_sigma_schedule_table4():
+    """Levels and labels as Table 4 prints them (levels as exact fractions,
+    labels to the printed digits), from both the oracle and the scalar
+    version written by another algebraic route."""
+    n = 0
+    for line in _golden_lines("sigma_schedule.txt"):
+        name, raw, num, den, label = line.split()
+        sigma = int(num) / int(den)
+        if raw != "-":
+            assert abs(float(O.shifted_sigma(int(raw))) - sigma) < 1e-15, name
+            assert abs(brute.shifted_sigma(int(raw)) - sigma) < 1e-15, name
+            printed = float(label)
+            assert abs(float(O.dit_label(sigma)) - printed) <= 0.05 + 1e-12, name
+        else:
+            assert float(label) == 0.0          # the clean-cache forward's label
+        n += 1
+    assert n == 6
+    # the 2-step schedule is a subset of the printed levels
+    assert np.allclose(O.shifted_sigma(O.RAW_STEPS_2), [1.0, 5.0 / 6.0], rtol=0, atol=1e-15)
+
+
+def _clean_sigma(name):
+    for line in _golden_lines("sigma_schedule.txt"):
+        f = line.split()
+        if f[0] == name:
+            return int(f[2]) / int(f[3])
+    raise KeyError(name)
+
+
+def test_sampler_forward_counts_table3():
+    """Running the sampler over a clip's seven chunks makes Table 3's forward
+    counts: 35 for Self Forcing (four steps per chunk), 23 for UnStep (two per
+    later chunk); each chunk ends with the label-0 clean-cache forward."""
+    rows = {l.split()[0]: l.split() for l in _golden_lines("clip_forwards.txt")}
+    for name, later, s_star in (("self_forcing", O.RAW_STEPS_4, _clean_sigma("clean_sf")),
+                                ("unstep", O.RAW_STEPS_2, _clean_sigma("clean_unstep"))):
+        _, chunks, first, later_n, _, total, _ = rows[name]
+        assert len(later) == int(later_n) and len(O.RAW_STEPS_4) == int(first)
+        calls = []
+        dit = lambda x, t: (calls.append(t), np.zeros_like(x))[1]
+        for c in range(int(chunks)):
+            steps = O.RAW_STEPS_4 if c == 0 else later
+            before = len(calls)
+            O.sample_chunk(dit, np.ones(4), [np.zeros(4)] * len(steps), steps, s_star)
+            assert calls[-1] == 0.0 and 0.0 not in calls[before:-1]
+        assert len(calls) == int(total), name
+
+
+def test_sampler_recovers_clean_latent_from_exact_velocity():
+    """A model that returns the exact velocity of the latent it is given
+    (v = eps - x0 for x = (1 - s) x0 + s eps) makes every step's estimate the
+    clean latent, so each chunk comes out as x0 after any schedule, at both
+    clean-cache levels; and the levels it sees are Table 4's, in order."""
+    rs = np.random.default_rng(3)
+    x0 = rs.standard_normal(50)
+    for steps, s_star in ((O.RAW_STEPS_4, 0.0), (O.RAW_STEPS_4, 0.02), (O.RAW_STEPS_2, 0.02)):
+        levels = [float(s) for s in O.shifted_sigma(steps)] + [s_star]
+        seen = []
+
+        def exact(x, t, _lv=levels, _seen=seen):
+            s = _lv[len(_seen)]
+            _seen.append(s)
+            return np.zeros_like(x) if s == 0 else (x - x0) / s
+
+        noises = [rs.standard_normal(50) for _ in steps]
+        out, lv, labels = O.sample_chunk(exact, rs.standard_normal(50), noises, steps, s_star)
+        assert np.max(np.abs(out - x0)) < 1e-12
+        assert lv == levels and labels == [1000.0 * s for s in levels[:-1]] + [0.0]
+
+
+def test_flow_step_level_endpoints():
+    """Table 4's endpoints: level 1 is pure noise and level 0 the clean
+    latent, so renoising to 1 gives the draw itself and to 0 the estimate;
+    at level 0 the estimate is the latent whatever the velocity."""
+    rs = np.random.default_rng(4)
+    x, v, eps = (rs.standard_normal(33) for _ in range(3))
+    x0, xn = O.flow_step(x, v, eps, 0.625, 1.0)
+    assert np.array_equal(xn, eps)
+    x0b, xn0 = O.flow_step(x, v, None, 0.625, 0.0)
+    assert np.array_equal(x0b, x0) and np.array_equal(xn0, x0)
+    assert np.array_equal(O.flow_step(x, v, eps, 0.0, 0.0)[0], x)
+
+
+def test_sampler_matches_scalar_brute_force():
+    """Oracle against the scalar sampler (another route for the mapping and
+    the renoising) with a fixed, input-independent velocity per forward."""
+    rs = np.random.default_rng(5)
+    n = 9
+    for steps, s_star in ((O.RAW_STEPS_4, 0.0), (O.RAW_STEPS_2, 0.02), ((1000, 750), 0.02)):
+        vs = [rs.standard_normal(n) for _ in range(len(steps) + 1)]
+        x_init = rs.standard_normal(n)
+        noises = [rs.standard_normal(n) for _ in steps]
+        it1, it2 = iter(vs), iter(vs)
+        a, la, ta = O.sample_chunk(lambda x, t: next(it1), x_init, noises, steps, s_star)
+        b, lb, tb = brute.sample_chunk(lambda x, t: next(it2).tolist(), x_init.tolist(),
+                                       [z.tolist() for z in noises], steps, s_star)
+        assert np.max(np.abs(a - np.array(b))) < 1e-12
+        assert np.allclose(la, lb, rtol=0, atol=1e-15) and np.allclose(ta, tb, rtol=0, atol=1e-12)
