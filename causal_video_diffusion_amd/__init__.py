@@ -11,4 +11,4 @@ from ._binding import (UstError, Geom, Kv, geom, kv, load, ust_v_row_len,  # noq
                        ust_rope_table_build, ust_kv_append, ust_window_attn,
                        ust_lowrank_proj, ust_slot_of_frame, ust_window_plan,
                        ust_window_attn_split, ust_window_attn_work_bytes,
-                       ust_qkv_append)
+                       ust_qkv_append, ust_flow_step, ust_sigma_schedule)

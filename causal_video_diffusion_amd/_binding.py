@@ -21,8 +21,8 @@ STATUS = {0: "UST_OK", 1: "UST_E_NULL", 2: "UST_E_SHAPE", 3: "UST_E_RANGE",
 # every entry point the header declares
 EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
            "ust_window_attn", "ust_window_attn_work_bytes", "ust_window_attn_split",
-           "ust_qkv_append", "ust_lowrank_proj", "ust_slot_of_frame", "ust_window_plan",
-           "ust_status_str", "ust_last_error")
+           "ust_qkv_append", "ust_lowrank_proj", "ust_flow_step", "ust_slot_of_frame",
+           "ust_window_plan", "ust_sigma_schedule", "ust_status_str", "ust_last_error")
 
 
 class UstError(RuntimeError):
@@ -70,6 +70,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         I32, P]),
         "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, P, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
+        "ust_flow_step": (I32, [P, P, P, F32, F32, P, P, ctypes.c_int64, P]),
+        "ust_sigma_schedule": (I32, [IP, I32, F64, I32, ctypes.POINTER(F64),
+                                     ctypes.POINTER(F64)]),
         "ust_slot_of_frame": (I32, [KP, I32]),
         "ust_window_plan": (I32, [GP, KP, I32, I32, IP, IP, I32, IP]),
         "ust_status_str": (ctypes.c_char_p, [I32]),
@@ -174,6 +177,22 @@ def ust_lowrank_proj(x, a, b, bias, t_work, y, M: int, K: int, r: int, N: int,
     _check(load().ust_lowrank_proj(_ptr(x), _ptr(a), _ptr(b), _ptr(bias),
                                    _ptr(t_work), _ptr(y), M, K, r, N,
                                    _stream(stream)))
+
+
+def ust_flow_step(x, v, noise, sigma: float, sigma_next: float, x0_out, x_next, n: int,
+                  stream=None) -> None:
+    _check(load().ust_flow_step(_ptr(x), _ptr(v), _ptr(noise), sigma, sigma_next,
+                                _ptr(x0_out), _ptr(x_next), n, _stream(stream)))
+
+
+def ust_sigma_schedule(raw_steps, shift: float = 5.0, n_train: int = 1000):
+    """(levels, labels) of the raw timesteps, as Python lists."""
+    n = len(raw_steps)
+    raw = (ctypes.c_int32 * max(n, 1))(*raw_steps)
+    sig = (ctypes.c_double * max(n, 1))()
+    lab = (ctypes.c_double * max(n, 1))()
+    _check(load().ust_sigma_schedule(raw, n, shift, n_train, sig, lab))
+    return list(sig[:n]), list(lab[:n])
 
 
 def ust_slot_of_frame(ring: Kv, frame: int) -> int:

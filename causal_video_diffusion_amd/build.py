@@ -21,7 +21,7 @@ OUT = os.path.join(PKG, "libust.so")
 OBJ = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["ust_host.cpp", "rope_table.hip", "kv_append.hip", "window_attn.hip",
+SOURCES = ["ust_host.cpp", "rope_table.hip", "kv_append.hip", "window_attn.hip", "sampler.hip",
            "gemm.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -1,6 +1,6 @@
 // RoPE the chunk's keys and append keys and values to the frame-slot ring
-// (UnStep, abstract: KV cache indexed by latent frame, fused RoPE with cached
-// coefficients).
+// (UnStep, abstract: the KV cache is indexed by latent frame, and RoPE is
+// applied from precomputed coefficients).
 //
 // One workgroup handles 64 tokens of one latent frame for one head:
 //   keys:   16-byte loads of k_new and of the table's cos/sin for four

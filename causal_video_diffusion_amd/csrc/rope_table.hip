@@ -1,5 +1,5 @@
-// Cached 3-D RoPE coefficients (UnStep, abstract: fused RoPE with cached
-// coefficients).  One thread per (frame, row, col, pair); angles in fp64,
+// Cached 3-D RoPE coefficients (UnStep, abstract: RoPE is applied from
+// precomputed coefficients).  One thread per (frame, row, col, pair); angles in fp64,
 // stored as fp32.  Runs once per geometry, so it is written for clarity.
 
 #include "ust_internal.h"

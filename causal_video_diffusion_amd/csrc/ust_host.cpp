@@ -437,4 +437,49 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const v
   }
 }
 
+ust_status ust_sigma_schedule(const int32_t* raw_steps, int32_t n, double shift,
+                              int32_t n_train, double* sigma_out, double* label_out) {
+  try {
+    if (!raw_steps || !sigma_out) return fail(UST_E_NULL, "raw_steps / sigma_out is NULL");
+    if (n < 0) return fail(UST_E_SHAPE, "n %d < 0", n);
+    if (!(shift > 0.0) || !std::isfinite(shift)) return fail(UST_E_RANGE, "shift must be > 0");
+    if (n_train <= 0) return fail(UST_E_RANGE, "n_train %d <= 0", n_train);
+    for (int32_t i = 0; i < n; ++i)
+      if (raw_steps[i] < 0 || raw_steps[i] > n_train)
+        return fail(UST_E_RANGE, "raw step %d outside [0, %d]", raw_steps[i], n_train);
+    for (int32_t i = 0; i < n; ++i) {
+      const double u = double(raw_steps[i]) / double(n_train);
+      const double sigma = shift * u / (1.0 + (shift - 1.0) * u);
+      sigma_out[i] = sigma;
+      if (label_out) label_out[i] = double(n_train) * sigma;
+    }
+    return ok();
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_flow_step(const float* x, const void* v, const float* noise, float sigma,
+                         float sigma_next, float* x0_out, float* x_next, int64_t n,
+                         hipStream_t stream) {
+  try {
+    if (!x || !v || !x_next) return fail(UST_E_NULL, "x, v or x_next is NULL");
+    if (sigma_next != 0.f && !noise)
+      return fail(UST_E_NULL, "noise is NULL but sigma_next is %g, not 0", double(sigma_next));
+    if (n < 0) return fail(UST_E_SHAPE, "n %lld < 0", static_cast<long long>(n));
+    if (!(sigma >= 0.f && sigma <= 1.f) || !(sigma_next >= 0.f && sigma_next <= 1.f))
+      return fail(UST_E_RANGE, "levels must lie in [0, 1] (got %g, %g)", double(sigma),
+                  double(sigma_next));
+    if (!aligned16(x) || !aligned16(v) || !aligned16(x_next) || (noise && !aligned16(noise)) ||
+        (x0_out && !aligned16(x0_out)))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    if (n == 0) return ok();
+    ust::FlowStepArgs a{x, static_cast<const uint16_t*>(v), sigma_next != 0.f ? noise : nullptr,
+                        x0_out, x_next, n, sigma, sigma_next, 1.0f - sigma_next};
+    return hip_status(ust::launch_flow_step(a, stream), "flow_step launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
 }  // extern "C"

@@ -75,7 +75,21 @@ struct QkvEpilogue {
   int32_t chunk_slot[8];     // slot of each chunk frame
 };
 
+// One sampler step: x0_hat = x - sigma v, x_next = keep x0_hat + sigma_next
+// noise (keep = 1 - sigma_next, rounded to fp32 by the caller); noise NULL
+// means sigma_next = 0 and x_next = x0_hat.  x0_out may be NULL.
+struct FlowStepArgs {
+  const float* x;            // [n]
+  const uint16_t* v;         // [n] bf16
+  const float* noise;        // [n] or nullptr
+  float* x0_out;             // [n] or nullptr
+  float* x_next;             // [n]
+  int64_t n;
+  float sigma, sigma_next, keep;
+};
+
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
+hipError_t launch_flow_step(const FlowStepArgs& a, hipStream_t s);
 // X [M][K] W [3HD][K]^T with the QKV epilogue; K % 64 == 0, D in {64, 128}
 hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);

@@ -274,3 +274,37 @@ def clip_forwards(n_chunks: int, first_steps: int, later_steps: int,
         if clean_pass:
             seq.append((c, n, True))
     return seq
+
+
+# ------------------------------------------------------------------ sampler
+
+SAMPLER_RAW_STEPS_4 = (1000, 750, 500, 250)   # the few-step model's four (Table 4)
+SAMPLER_RAW_STEPS_2 = (1000, 500)             # an UnStep later chunk's two (a reading)
+
+
+def sample_chunk(dit, x: torch.Tensor, noises, raw_steps, sigma_star: float,
+                 shift: float = 5.0):
+    """One chunk of the sampler on the device (UnStep, Tables 3 and 4).
+
+    A denoising forward per raw step, each followed by ust_flow_step, which
+    renoises to the next level (the last step to sigma_star). Then come the
+    label-0 clean-cache forward and its step to level 0. dit(x, t) returns the
+    velocity as a bf16 device tensor shaped like x, for latent x at label t.
+    x is the chunk's initial noise, fp32 on the device; it is updated in
+    place. noises[i] is the fp32 draw for the renoising after step i (unused
+    when that level is 0). Returns (x, the levels of the forwards, the labels
+    passed)."""
+    levels, labels = B.ust_sigma_schedule(list(raw_steps), shift)
+    n = x.numel()
+    seen, passed = [], []
+    for i, (s, t) in enumerate(zip(levels, labels)):
+        nxt = levels[i + 1] if i + 1 < len(levels) else float(sigma_star)
+        v = dit(x, t)
+        seen.append(s)
+        passed.append(t)
+        B.ust_flow_step(x, v, noises[i] if nxt != 0 else None, s, nxt, None, x, n)
+    v = dit(x, 0.0)
+    seen.append(float(sigma_star))
+    passed.append(0.0)
+    B.ust_flow_step(x, v, None, float(sigma_star), 0.0, None, x, n)
+    return x, seen, passed

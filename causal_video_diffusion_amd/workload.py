@@ -37,6 +37,10 @@ TAG_WQ = 5
 TAG_WK = 6
 TAG_WV = 7
 TAG_WO = 8
+TAG_EPS = 9     # the sampler's noise draws
+TAG_VEL = 10    # stand-in DiT velocities for the sampler
+
+LATENT_CHANNELS = 16   # appendix Table 3: initial noise 1x21x16x60x104
 
 
 @dataclass(frozen=True)
@@ -177,6 +181,26 @@ def chunk_tokens(w: Workload, tag: int, chunk: int, step: int = 0, layer: int = 
     Token n of the chunk is latent frame chunk*C + n // T, position
     (y, x) = divmod(n % T, grid_w) in that frame."""
     return normal_bf16(w, (w.n_q, w.n_heads, w.head_dim), tag, chunk, step, layer)
+
+
+def latent_shape(w: Workload):
+    """A chunk's latent: chunk_frames x 16 channels x (2 grid_h) x (2 grid_w);
+    each token is a 1x2x2 patch (appendix Table 3: 21 x 16 x 60 x 104 for
+    the 832x480 clip, whose frames are 30 x 52 tokens)."""
+    return (w.chunk_frames, LATENT_CHANNELS, 2 * w.grid_h, 2 * w.grid_w)
+
+
+def latent_noise(w: Workload, chunk: int, draw: int) -> np.ndarray:
+    """A chunk's noise draw `draw` (0: its initial noise; i + 1: the draw for
+    renoising after its step i), N(0, 1) in float32, flat."""
+    g = rng(w, TAG_EPS, chunk, draw, 0)
+    return g.standard_normal(size=int(np.prod(latent_shape(w))), dtype=np.float32)
+
+
+def stand_in_velocity(w: Workload, chunk: int, forward: int) -> np.ndarray:
+    """A velocity for the sampler when no DiT is run: N(0, 1) drawn in
+    float32, rounded to bf16 (uint16 bits), flat, per (chunk, forward)."""
+    return normal_bf16(w, (int(np.prod(latent_shape(w))),), TAG_VEL, chunk, forward, 0)
 
 
 def activations(w: Workload, chunk: int, step: int = 0):

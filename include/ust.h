@@ -22,6 +22,9 @@
  *                         the K/V append fused into the product's epilogue
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
+ *   ust_flow_step         one step of the chunk sampler: denoised estimate and
+ *                         renoising (Table 4; abstract)
+ *   ust_sigma_schedule    the sampler's noise levels (host only; Table 4)
  *
  * Conventions (all entry points):
  *  - Device pointers are caller-owned.  The library never allocates, frees
@@ -103,8 +106,8 @@ typedef struct ust_kv {
  * of 64.  Returns -1 if T <= 0. */
 int32_t ust_v_row_len(int32_t tokens_per_frame);
 
-/* Build the cached RoPE coefficients (abstract: fused RoPE with cached
- * coefficients).  For every frame f < n_frames, row y, column x and pair p,
+/* Build the cached RoPE coefficients (abstract: RoPE is applied from
+ * precomputed coefficients).  For every frame f < n_frames, row y, column x and pair p,
  * angle = pos * theta^(-j/n) with (pos, j, n) given by p's axis as in
  * ust_geom; computed in fp64 and rounded to fp32.
  *   cos_out, sin_out: fp32 [n_frames][grid_h][grid_w][head_dim/2], written.
@@ -241,7 +244,54 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b,
                             int32_t M, int32_t K, int32_t r, int32_t N,
                             hipStream_t stream);
 
+/* One step of the chunk sampler (Table 4: the noise levels of the denoising
+ * steps and of the clean-cache forward; abstract: the generated frames are
+ * renoised to a nearly clean level and the clean-cache forward refines
+ * them).  With a latent at level sigma written (1 - sigma) x0 + sigma eps and
+ * the DiT's output the velocity eps - x0 (flow matching, the parameterisation
+ * of this model family), for every i < n:
+ *   x0_hat[i] = x[i] - sigma v[i]                  (fp32, one fused multiply-add)
+ *   x_next[i] = keep x0_hat[i] + sigma_next noise[i]  (keep = fp32(1 - sigma_next):
+ *                                          the product rounded, then one fma)
+ * and x_next = x0_hat exactly when sigma_next == 0 (noise is then not read).
+ * A chunk's denoising steps run at the levels of ust_sigma_schedule, each
+ * renoising to the next level with a fresh draw; the last one renoises to
+ * the clean-cache level sigma* (0.02 for UnStep, 0 for Self Forcing); the
+ * clean-cache forward's step (sigma = sigma*, sigma_next = 0) gives the chunk
+ * kept.
+ *   x:      fp32 [n] latent at level sigma, read.
+ *   v:      bf16 [n] velocity from the DiT, read.
+ *   noise:  fp32 [n] draw for the renoising, read; may be NULL when
+ *           sigma_next == 0.  Random numbers are the caller's: the library
+ *           draws none.
+ *   x0_out: fp32 [n] or NULL: receives x0_hat.
+ *   x_next: fp32 [n]: receives the renoised latent.
+ *   Each output element depends only on the inputs at its own index, so an
+ *   output may be the same buffer as an input (no partial overlap).
+ * Errors: x, v or x_next NULL, or noise NULL with sigma_next != 0
+ * (UST_E_NULL); n < 0 (UST_E_SHAPE); a level outside [0, 1] or NaN
+ * (UST_E_RANGE); a pointer not 16-byte aligned (UST_E_ALIGN).  n == 0
+ * launches nothing. */
+ust_status ust_flow_step(const float* x, const void* v, const float* noise, float sigma,
+                         float sigma_next, float* x0_out, float* x_next, int64_t n,
+                         hipStream_t stream);
+
 /* ---- host-only helpers (no GPU needed) ---- */
+
+/* Noise levels of raw timesteps after the shift mapping (Table 4, shift 5,
+ * n_train 1000: raw 1000, 750, 500, 250 give 1, 15/16, 5/6, 5/8):
+ *   u = raw / n_train,  sigma = shift u / (1 + (shift - 1) u),  in fp64,
+ * and the DiT's timestep label n_train sigma.  A Self Forcing chunk steps
+ * through raw 1000, 750, 500, 250; an UnStep later chunk through two of
+ * them (1000 and 500 in this library's workloads: the pages do not say
+ * which two).
+ *   raw_steps: [n] host array, each in [0, n_train].
+ *   sigma_out: [n] host array, written.  label_out: [n] host array or NULL.
+ * Errors: NULL raw_steps / sigma_out (UST_E_NULL); n < 0 (UST_E_SHAPE);
+ * shift <= 0 or not finite, n_train <= 0, a raw step outside [0, n_train]
+ * (UST_E_RANGE). */
+ust_status ust_sigma_schedule(const int32_t* raw_steps, int32_t n, double shift,
+                              int32_t n_train, double* sigma_out, double* label_out);
 
 /* Ring slot of latent frame `frame`; -1 if frame < 0 or the ring is invalid
  * (n_sink < 0 or n_slots <= n_sink). */

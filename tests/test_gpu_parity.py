@@ -422,6 +422,86 @@ def test_v_one_gives_one_and_k_zero_gives_mean():
     assert np.max(np.abs(lse - math.log(len(frames) * w.T))) < 1e-4
 
 
+# ------------------------------------------------------------------ sampler
+# One step in fp32: x0 = x - sigma v (one rounding), x_next = fp32(1 - s')
+# x0 rounded, then + s' eps in one fma; the oracle is fp64 with the same fp32
+# levels.  Each rounding is at most 2^-24 relative, so per element
+# |error| <= 2^-21 (|x| + |sigma v| + |s' eps|), generously.
+
+def _flow_bound(x, sv, se):
+    return 2.0 ** -21 * (np.abs(x) + np.abs(sv) + np.abs(se)) + 1e-30
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1001, 3 * 16 * 60 * 104])
+def test_flow_step_matches_oracle(n):
+    """Against the fp64 oracle at Table 4's levels (and the clean-cache ones),
+    sizes with ragged tails up to the Wan chunk latent; the exact cases bit
+    for bit; in place equal to out of place; nothing past n written."""
+    print(f"[flow_step n={n}]", flush=True)
+    rs = np.random.default_rng(n)
+    x = (rs.standard_normal(n) * 2).astype(np.float32)
+    vb = wl.f32_to_bf16_bits(rs.standard_normal(n).astype(np.float32))
+    eps = rs.standard_normal(n).astype(np.float32)
+    v = _f64(vb)
+    xd, vd, ed = torch.from_numpy(x).cuda(), P.to_device_bf16(vb), torch.from_numpy(eps).cuda()
+    for s, sn in ((1.0, 0.9375), (5 / 6, 0.625), (0.625, 0.02), (0.02, 0.0), (0.0, 0.0),
+                  (0.5, 1.0)):
+        s32, sn32 = float(np.float32(s)), float(np.float32(sn))
+        x0 = torch.full((n + 8,), float("nan"), device="cuda")
+        xn = torch.full((n + 8,), float("nan"), device="cuda")
+        B.ust_flow_step(xd, vd, ed, s32, sn32, x0, xn, n)
+        torch.cuda.synchronize()
+        g0, gn = x0.cpu().numpy(), xn.cpu().numpy()
+        assert np.isnan(g0[n:]).all() and np.isnan(gn[n:]).all(), "wrote past n"
+        g0, gn = g0[:n], gn[:n]
+        r0, rn = O.flow_step(x, v, eps, s32, sn32)
+        assert np.all(np.abs(g0 - r0) <= _flow_bound(x, s32 * v, 0)), f"x0 {s}->{sn}"
+        assert np.all(np.abs(gn - rn) <= _flow_bound(x, s32 * v, sn32 * eps)), f"x_next {s}->{sn}"
+        if sn == 0.0:
+            assert np.array_equal(gn, g0)
+        if s == 0.0:
+            assert np.array_equal(g0, x)
+        if sn == 1.0:
+            assert np.array_equal(gn, eps)
+        # in place: the latent overwritten by its successor
+        xi = xd.clone()
+        B.ust_flow_step(xi, vd, ed, s32, sn32, None, xi, n)
+        torch.cuda.synchronize()
+        assert np.array_equal(xi.cpu().numpy(), gn), f"in place {s}->{sn}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan_window"])
+def test_sample_chunk_matches_oracle(name):
+    """Whole chunks of the sampler against the oracle's: Self Forcing's four
+    steps with sigma* = 0, UnStep's two with sigma* = 0.02, and four with
+    0.02, each with stand-in velocities drawn per forward (the same on both
+    sides).  Errors add up over the forwards: per element at most
+    (forwards) 2^-21 times the sum of every input's magnitude there."""
+    w = wl.ALL[name]
+    cases = ((P.SAMPLER_RAW_STEPS_4, 0.0), (P.SAMPLER_RAW_STEPS_2, 0.02),
+             (P.SAMPLER_RAW_STEPS_4, 0.02))
+    for c, (steps, s_star) in enumerate(cases):
+        print(f"[sample_chunk {name} steps {steps} sigma* {s_star}]", flush=True)
+        x_init = wl.latent_noise(w, c, 0)
+        noises = [wl.latent_noise(w, c, i + 1) for i in range(len(steps))]
+        vels = [wl.stand_in_velocity(w, c, f) for f in range(len(steps) + 1)]
+        x = torch.from_numpy(x_init.copy()).cuda()
+        it = iter([P.to_device_bf16(b) for b in vels])
+        got, lv, lb = P.sample_chunk(lambda xx, t: next(it), x,
+                                     [torch.from_numpy(z).cuda() for z in noises], steps, s_star)
+        torch.cuda.synchronize()
+        it2 = iter(vels)
+        ref, lv2, lb2 = O.sample_chunk(lambda xx, t: _f64(next(it2)), x_init, noises, steps,
+                                       s_star)
+        assert np.allclose(lv, lv2, rtol=1e-15, atol=0) and np.allclose(lb, lb2, rtol=1e-15, atol=0)
+        assert len(lv) == len(steps) + 1 and lb[-1] == 0.0
+        mag = np.abs(x_init.astype(np.float64)) + sum(np.abs(_f64(b)) for b in vels) + \
+            sum(np.abs(z.astype(np.float64)) for z in noises)
+        err = np.abs(got.cpu().numpy() - ref)
+        assert np.all(err <= (len(steps) + 1) * 2.0 ** -21 * mag + 1e-30), \
+            f"max err {err.max():.3e}"
+
+
 # ------------------------------------------------------------------ low rank
 
 @pytest.mark.parametrize("name,M", [("tiny", 72), ("mid", 312), ("mid", 100),

@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import causal_video_diffusion_amd as cvd
@@ -34,7 +35,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 12
+    assert len(syms) == 14
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -223,6 +224,41 @@ def test_qkv_append_rejects_bad_arguments(lib):
     small = B.Kv(fake, fake, 4, 3)
     assert _raw(lib, "ust_qkv_append", gp, ctypes.byref(small), fake, fake, 1536, fake, fake,
                 21, 6, fake, None)[0] == "UST_E_RANGE"
+
+
+def test_flow_step_rejects_bad_arguments(lib):
+    """Each call fails in validation, before any launch (no GPU needed)."""
+    fake = 0x10000
+    call = lambda x, v, nz, s, sn, x0, xn, n: _raw(lib, "ust_flow_step", x, v, nz, s, sn, x0,
+                                                 xn, n, None)
+    assert call(None, fake, fake, 0.5, 0.25, None, fake, 8)[0] == "UST_E_NULL"
+    assert call(fake, None, fake, 0.5, 0.25, None, fake, 8)[0] == "UST_E_NULL"
+    assert call(fake, fake, fake, 0.5, 0.25, None, None, 8)[0] == "UST_E_NULL"
+    assert call(fake, fake, None, 0.5, 0.25, None, fake, 8)[0] == "UST_E_NULL"   # noise needed
+    assert call(fake, fake, fake, 0.5, 0.25, None, fake, -1)[0] == "UST_E_SHAPE"
+    assert call(fake, fake, fake, 1.5, 0.25, None, fake, 8)[0] == "UST_E_RANGE"
+    assert call(fake, fake, fake, 0.5, -0.1, None, fake, 8)[0] == "UST_E_RANGE"
+    assert call(fake, fake, fake, float("nan"), 0.0, None, fake, 8)[0] == "UST_E_RANGE"
+    assert call(fake + 4, fake, fake, 0.5, 0.25, None, fake, 8)[0] == "UST_E_ALIGN"
+    assert call(fake, fake, fake, 0.5, 0.25, fake + 8, fake, 8)[0] == "UST_E_ALIGN"
+    assert call(fake, fake, None, 0.5, 0.0, None, fake, 0)[0] == "UST_OK"   # nothing to do
+
+
+def test_sigma_schedule_matches_oracle_and_table4(lib):
+    """The library's levels and labels against the oracle (same closed form in
+    fp64, to rounding) and Table 4's printed fractions; argument errors."""
+    raw = [1000, 750, 500, 250, 0]
+    sig, lab = B.ust_sigma_schedule(raw)
+    ref = O.shifted_sigma(raw)
+    assert np.allclose(sig, ref, rtol=1e-15, atol=0)
+    assert np.allclose(lab, O.dit_label(ref), rtol=1e-15, atol=0)
+    assert sig[:4] == [1.0, 15 / 16, pytest.approx(5 / 6, rel=1e-15), 5 / 8] and sig[4] == 0.0
+    arr = (ctypes.c_int32 * 2)(1000, 1001)
+    out = (ctypes.c_double * 2)()
+    assert _raw(lib, "ust_sigma_schedule", arr, 2, 5.0, 1000, out, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_sigma_schedule", arr, 1, 0.0, 1000, out, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_sigma_schedule", None, 1, 5.0, 1000, out, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_sigma_schedule", arr, -1, 5.0, 1000, out, None)[0] == "UST_E_SHAPE"
 
 
 def test_window_attn_work_bytes(lib):
