@@ -48,12 +48,17 @@ ATTN_TRAFFIC_BYTES = {
     ("wan_window", "whole"): (2 * 109091 + 17699) * 1024,
     ("wan_720p", "split"): (2 * (590041 + 17004) + 62659 + 204) * 1024,   # attention + merge
 }
+# the sampler's flow step at the Wan chunk latent, per launch averaged over
+# one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
+# clean-cache ones do not: 892 KiB; every one writes 1170 KiB), same scaling
+SAMPLER_TRAFFIC_BYTES = round((2 * (16 * 1478 + 7 * 892) / 23 + 1170) * 1024)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip", "wan_fused"),
+    ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip", "wan_fused",
+                                            "wan_sampler"),
                     default="wan_window",
                     help="the windowed Wan2.1-1.3B layer-chunk (default); the same layer "
                          "at 720p (45x80 tokens/frame, rank 256); the whole 81-frame "
@@ -101,6 +106,8 @@ def main():
         return main_clip(args)
     if args.workload == "wan_fused":
         return main_fused(args)
+    if args.workload == "wan_sampler":
+        return main_sampler(args)
     w = wl.ALL[args.workload]
     C = 5                                   # last chunk prepared
     # Steady-state chunks timed in turn.  The windowed layer's 21-slot ring
@@ -410,6 +417,157 @@ def main_fused(args):
         "stages_note": "separate untimed pass with events between the stages (each event "
                        "adds ~2-3 us; stage times include launch gaps)",
     }
+    print(json.dumps(result), flush=True)
+
+
+def main_sampler(args):
+    """The chunk sampler over one UnStep clip (Tables 3 and 4): 7 chunks of
+    the Wan latent (3 x 16 x 60 x 104 fp32 each); chunk 0 takes four
+    denoising steps, the later chunks two, and each chunk then the
+    clean-cache step (sigma* = 0.02), 23 ust_flow_step launches per clip.
+    No DiT runs: each forward's velocity is a pre-drawn bf16 stand-in, so the
+    step is the sampler's own HBM traffic.  A step is one clip."""
+    import numpy as np
+    import torch
+
+    from causal_video_diffusion_amd import _binding as B
+    from causal_video_diffusion_amd import path as P
+    from causal_video_diffusion_amd import workload as wl
+
+    w = wl.WAN_CLIP
+    n = int(np.prod(wl.latent_shape(w)))
+    n_chunks, s_star = 7, 0.02
+    plan = []                   # (chunk, forward, sigma, sigma_next) in clip order
+    for c in range(n_chunks):
+        steps = P.SAMPLER_RAW_STEPS_4 if c == 0 else P.SAMPLER_RAW_STEPS_2
+        levels, _ = B.ust_sigma_schedule(list(steps))
+        for i, sg in enumerate(levels):
+            plan.append((c, i, sg, levels[i + 1] if i + 1 < len(levels) else s_star))
+        plan.append((c, len(levels), s_star, 0.0))
+    assert len(plan) == 23
+    lat0 = [torch.from_numpy(wl.latent_noise(w, c, 0)).cuda() for c in range(n_chunks)]
+    lat = [t.clone() for t in lat0]
+    noise = [[torch.from_numpy(wl.latent_noise(w, c, i + 1)).cuda() for i in range(4)]
+             for c in range(n_chunks)]
+    vel = [[P.to_device_bf16(wl.stand_in_velocity(w, c, f)) for f in range(5)]
+           for c in range(n_chunks)]
+    # algorithmic bytes: x (4 B) and v (2 B) read, x_next (4 B) written, and
+    # the noise (4 B) read when renoising to a level above 0
+    nbytes = [n * (14 if sn != 0 else 10) for (_, _, _, sn) in plan]
+    stream = torch.cuda.current_stream()
+
+    def clip():
+        for (c, f, sg, sn) in plan:
+            B.ust_flow_step(lat[c], vel[c][f], noise[c][f] if sn != 0 else None, sg, sn, None,
+                            lat[c], n)
+
+    for _ in range(args.warmup):
+        clip()
+    for t, t0 in zip(lat, lat0):
+        t.copy_(t0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        clip()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    # the same clip captured in a HIP graph (no memset nodes) and replayed:
+    # the launch cost a DiT pipeline that captures its forwards would see
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        clip()
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        clip()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_clip = e0.elapsed_time(e1) / args.steps
+    us_per_launch = 1000.0 * ms_per_clip / len(plan)
+    gbs = sum(nbytes) / (ms_per_clip * 1e-3) / 1e9
+    # the same kernel over all seven chunks' latents at once (29 MB): its rate
+    # away from the launch-latency regime of one 1.2 MB chunk
+    big = torch.cat(lat0)
+    bv = torch.cat([vel[c][0] for c in range(n_chunks)])
+    bz = torch.cat([noise[c][0] for c in range(n_chunks)])
+    for _ in range(5):
+        B.ust_flow_step(big, bv, bz, 0.9375, 0.8333333, None, big, big.numel())
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(50):
+        B.ust_flow_step(big, bv, bz, 0.9375, 0.8333333, None, big, big.numel())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    big_us = 1000.0 * e0.elapsed_time(e1) / 50
+    big_gbs = big.numel() * 14 / (big_us * 1e-6) / 1e9
+    result = {
+        "metric": "chunk-sampler step GB/s (ust_flow_step at the Wan chunk latent), % HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_clip, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "wan_sampler: one UnStep clip of the chunk sampler, 7 chunks of the Wan "
+                        "latent 3x16x60x104 fp32 (299520 elements); 4 denoising steps for chunk "
+                        "0, 2 for each later chunk, then each chunk's clean-cache step at "
+                        "sigma* 0.02: 23 flow steps; velocities pre-drawn (no DiT); a step is "
+                        "one clip, replayed from a HIP graph",
+            "latent_elems": n, "launches_per_clip": len(plan),
+            "bytes_per_clip": int(sum(nbytes)),
+            "eager_ms_per_clip": round(eager_ms, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": SAMPLER_TRAFFIC_BYTES,
+            "kernel": "flow_step_kernel (23 graph-replayed launches, per-launch average "
+                      "including the gaps between them)",
+            "kernel_us": round(us_per_launch, 2),
+        },
+        "all_chunks_at_once": {
+            "elems": int(big.numel()), "us": round(big_us, 2), "GBs": round(big_gbs, 1),
+            "hbm_frac": round(big_gbs / PEAK_HBM_GBS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        cpu_lat = [wl.latent_noise(w, c, 0).astype(np.float64) for c in range(n_chunks)]
+        cpu_noise = [[wl.latent_noise(w, c, i + 1) for i in range(4)] for c in range(n_chunks)]
+        cpu_vel = [[wl.bf16_bits_to_f64(wl.stand_in_velocity(w, c, f)) for f in range(5)]
+                   for c in range(n_chunks)]
+        t0 = time.perf_counter()
+        reps = 2
+        for _ in range(reps):
+            for (c, f, sg, sn) in plan:
+                _, cpu_lat[c] = O.flow_step(cpu_lat[c], cpu_vel[c][f],
+                                            cpu_noise[c][f] if sn != 0 else None, sg, sn)
+        cpu_s = (time.perf_counter() - t0) / reps
+        result["cpu_baseline"] = {
+            "value": round(sum(nbytes) / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "ms_per_step": round(cpu_s * 1e3, 1),
+            "sample": f"the whole clip's 23 flow steps in fp64 NumPy, {reps} times; value = the "
+                      "same algorithmic bytes / wall time (elementwise NumPy is single-threaded)",
+        }
     print(json.dumps(result), flush=True)
 
 

@@ -502,6 +502,59 @@ def test_sample_chunk_matches_oracle(name):
             f"max err {err.max():.3e}"
 
 
+def test_sampler_graph_replay_matches_eager():
+    """Three chunks of the UnStep sampler (4 + 1, 2 + 1, 2 + 1 flow steps)
+    captured in a HIP graph (kernel nodes only) and replayed three times,
+    with a reset of the latents and other eager work between replays: each
+    replay equals the eager run bit for bit."""
+    w = wl.WAN_WINDOW
+    n = int(np.prod(wl.latent_shape(w)))
+    plan = []
+    for c in range(3):
+        steps = P.SAMPLER_RAW_STEPS_4 if c == 0 else P.SAMPLER_RAW_STEPS_2
+        lv, _ = B.ust_sigma_schedule(list(steps))
+        plan += [(c, i, s, lv[i + 1] if i + 1 < len(lv) else 0.02) for i, s in enumerate(lv)]
+        plan.append((c, len(lv), 0.02, 0.0))
+    lat0 = [torch.from_numpy(wl.latent_noise(w, c, 0)).cuda() for c in range(3)]
+    lat = [t.clone() for t in lat0]
+    noise = [[torch.from_numpy(wl.latent_noise(w, c, i + 1)).cuda() for i in range(4)]
+             for c in range(3)]
+    vel = [[P.to_device_bf16(wl.stand_in_velocity(w, c, f)) for f in range(5)] for c in range(3)]
+
+    def clip():
+        for c, f, sg, sn in plan:
+            B.ust_flow_step(lat[c], vel[c][f], noise[c][f] if sn != 0 else None, sg, sn, None,
+                            lat[c], n)
+
+    def reset():
+        for t, t0 in zip(lat, lat0):
+            t.copy_(t0)
+
+    reset()
+    clip()
+    torch.cuda.synchronize()
+    ref = [t.cpu().numpy() for t in lat]
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        clip()
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        clip()
+    for r in range(3):
+        print(f"[sampler graph replay {r}]", flush=True)
+        reset()
+        junk = torch.randn(1 << 16, device="cuda").abs().sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) > 0
+        for c in range(3):
+            assert np.array_equal(lat[c].cpu().numpy(), ref[c]), f"replay {r} chunk {c}"
+
+
 # ------------------------------------------------------------------ low rank
 
 @pytest.mark.parametrize("name,M", [("tiny", 72), ("mid", 312), ("mid", 100),
