@@ -577,7 +577,10 @@ def main_clip(args):
     clean-cache forward; 23 forwards x 30 layers = 690 layer-chunks, each
     with its own weights and KV ring, in one stream.  Per layer-chunk: dense
     Q and K projections (harness support, reported apart), then the path.
-    A step is one whole clip."""
+    After each forward, the sampler steps the chunk's latent (ust_flow_step
+    at Table 4's levels, the clean-cache one at sigma* = 0.02); its velocity
+    is a pre-drawn stand-in, since the layers' outputs are not one.  A step
+    is one whole clip."""
     import numpy as np
     import torch
 
@@ -612,6 +615,21 @@ def main_clip(args):
               for (c, _, _) in sched]
     flops = sum(w.layers * attn_flops(w.n_q, nk, w.head_dim, w.n_heads) for nk in n_keys)
     n_lc = len(sched) * w.layers
+    # the sampler on each chunk's latent: (sigma, sigma_next) per forward
+    n_lat = int(np.prod(wl.latent_shape(w)))
+    s_star = 0.02
+    samp = []
+    for (c, i, clean) in sched:
+        steps = P.SAMPLER_RAW_STEPS_4 if (c == 0 or w.later_steps == 4) else P.SAMPLER_RAW_STEPS_2
+        lv, _ = B.ust_sigma_schedule(list(steps))
+        if clean:
+            samp.append((s_star, 0.0))
+        else:
+            samp.append((lv[i], lv[i + 1] if i + 1 < len(lv) else s_star))
+    lat = [torch.from_numpy(wl.latent_noise(w, c, 0)).cuda() for c in range(w.n_chunks)]
+    lat_noise = [[torch.from_numpy(wl.latent_noise(w, c, i + 1)).cuda() for i in range(4)]
+                 for c in range(w.n_chunks)]
+    lat_vel = [P.to_device_bf16(wl.stand_in_velocity(w, c, i)) for (c, i, _) in sched]
 
     def attention(ring, c):
         if bufs.attn_work is not None:
@@ -646,6 +664,10 @@ def main_clip(args):
                 if e:
                     e[4].record(stream)
                     ev.append(e)
+            sg, sn = samp[fi]
+            i = sched[fi][1]
+            B.ust_flow_step(lat[c], lat_vel[fi], lat_noise[c][i] if sn != 0 else None, sg, sn,
+                            None, lat[c], n_lat)
 
     print("[bench clip] warm-up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -687,8 +709,10 @@ def main_clip(args):
                         f"forward per chunk) x {w.layers} layers = {n_lc} layer-chunks; each "
                         f"Wan2.1-1.3B self-attention layer-chunk with dense Q/K projections, "
                         f"rank-{w.rank} V/O, window {w.n_sink} sink + {w.n_recent} recent + 3 "
-                        f"current frames, {w.n_slots}-slot ring per layer; a step is one clip",
+                        f"current frames, {w.n_slots}-slot ring per layer; the chunk sampler "
+                        f"steps each chunk's latent after each forward; a step is one clip",
             "layer_chunks": n_lc, "attn_tflop_per_clip": round(flops / 1e12, 2),
+            "sampler_steps": len(samp),
             "schedule": schedule,
         },
         "roofline": {
