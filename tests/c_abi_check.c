@@ -8,7 +8,12 @@
  *    softmax row sums to 1), to the rounding of the bf16 probabilities;
  *  - on random inputs the key-split schedule (5 workgroups) agrees with the
  *    one-workgroup-per-tile schedule within the bf16 bar, and both are finite;
- *  - ust_window_attn_work_bytes matches its stated formula.
+ *  - ust_window_attn_work_bytes matches its stated formula;
+ *  - ust_sigma_schedule gives the shift-5 levels 1 and 5/6 for raw 1000 and
+ *    500, and ust_flow_step matches a double-precision loop within fp32
+ *    rounding (2^-21 of the magnitudes involved: four roundings at most),
+ *    for a size with a ragged tail, and rejects a NULL noise when it would
+ *    be read.
  * Prints "ok" or the first failure and exits 1.
  */
 #include <math.h>
@@ -136,6 +141,43 @@ int main(void) {
         if (fabs((double)a - b) > max_d) max_d = fabs((double)a - b);
       }
       EXPECT(max_d <= 2e-2, "split vs unsplit differ by %g (pass %d chunk %d)", max_d, pass, c);
+    }
+  }
+  /* the sampler step */
+  {
+    const int32_t raw[2] = {1000, 500};
+    double sig[2], lab[2];
+    UST_OK_(ust_sigma_schedule(raw, 2, 5.0, 1000, sig, lab));
+    EXPECT(sig[0] == 1.0 && fabs(sig[1] - 5.0 / 6.0) < 1e-15 && fabs(lab[1] - 2500.0 / 3.0) < 1e-12,
+           "sigma schedule %g %g", sig[0], sig[1]);
+    enum { NS = 1001 };
+    float hx[NS], he[NS], hn[NS];
+    uint16_t hvb[NS];
+    for (int i = 0; i < NS; ++i) {
+      hx[i] = 2.0f * uniform_pm1();
+      he[i] = uniform_pm1();
+      hvb[i] = to_bf16(uniform_pm1());
+    }
+    float *dx, *de, *dn;
+    void* dv;
+    HIP_OK(hipMalloc((void**)&dx, sizeof(hx)));
+    HIP_OK(hipMalloc((void**)&de, sizeof(he)));
+    HIP_OK(hipMalloc((void**)&dn, sizeof(hn)));
+    HIP_OK(hipMalloc(&dv, sizeof(hvb)));
+    HIP_OK(hipMemcpy(dx, hx, sizeof(hx), hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(de, he, sizeof(he), hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(dv, hvb, sizeof(hvb), hipMemcpyHostToDevice));
+    const float s = (float)sig[1], sn = 0.02f;
+    EXPECT(ust_flow_step(dx, dv, NULL, s, sn, NULL, dn, NS, 0) == UST_E_NULL, "NULL noise accepted");
+    UST_OK_(ust_flow_step(dx, dv, de, s, sn, NULL, dn, NS, 0));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(hn, dn, sizeof(hn), hipMemcpyDeviceToHost));
+    for (int i = 0; i < NS; ++i) {
+      const double v = from_bf16(hvb[i]);
+      const double x0 = (double)hx[i] - (double)s * v;
+      const double ref = (1.0 - (double)sn) * x0 + (double)sn * he[i];
+      const double mag = fabs((double)hx[i]) + fabs((double)s * v) + fabs((double)sn * he[i]);
+      EXPECT(fabs(hn[i] - ref) <= ldexp(mag, -21), "flow step %d: %g vs %g", i, hn[i], ref);
     }
   }
   printf("ok\n");
