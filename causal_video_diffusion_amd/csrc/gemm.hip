@@ -150,8 +150,11 @@ gemm_nt_kernel(GemmArgs g) {
 // and the stage slice kt - 1 used is free to be refilled.  Rows past M or N
 // load clamped (finite) rows whose results are never stored.
 //
-// Tiles are BM x BN with 4 waves in a 2 x 2 grid; the launcher picks the
-// shape so that one round of workgroups (one per CU) covers the output.  The
+// Tiles are BM x BN over a WM x WN grid of waves.  With 8 waves (4 x 2), two
+// share each SIMD and cover each other's load-issue stalls with MFMAs; the
+// launcher uses 8-wave 256 x 128 tiles for wide outputs and 128 x 128 for the
+// narrow rank-r ones, and 4-wave 192 x 64 tiles for the 64-wide heads of the
+// fused projection.  The
 // workgroup -> tile map is XCD-aware: workgroups are dealt to the 8 XCDs
 // round-robin, and each XCD gets a contiguous, row-major run of tiles, so the
 // tiles that share rows of X run on one XCD and find them in its L2.
@@ -188,16 +191,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // QKV: the fused Q/K/V projection epilogue (QkvEpilogue) instead of Y.
-template <int BM, int BN, int STAGES, bool QKV>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// WM x WN waves (4 or 8); with 8, two waves share each SIMD, so one wave's
+// load-issue stalls are covered by the other's MFMAs.
+template <int BM, int BN, int STAGES, bool QKV, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
-  constexpr int MB = BM / 64;              // 32-row blocks of X per wave
-  constexpr int NB = BN / 64;              // 32-row blocks of W per wave
+  constexpr int NW = WM * WN;
+  constexpr int NT = 64 * NW;
+  constexpr int MB = BM / (32 * WM);       // 32-row blocks of X per wave
+  constexpr int NB = BN / (32 * WN);       // 32-row blocks of W per wave
+  static_assert(MB * 32 * WM == BM && NB * 32 * WN == BN, "tile splits over the wave grid");
   constexpr int FR = NB + MB;              // fragments per 16-wide k substep
   constexpr int NMMA = NB * MB;            // MFMAs per substep
   constexpr int XI = BM / 8, WI = BN / 8;  // 1 KB loads per slice for X and W
-  constexpr int NLD = (XI + WI) / 4;       // loads per wave per slice
-  static_assert((XI + WI) % 4 == 0, "loads split evenly over 4 waves");
+  constexpr int NLD = (XI + WI) / NW;      // loads per wave per slice
+  static_assert((XI + WI) % NW == 0, "loads split evenly over the waves");
   constexpr int STAGE = (BM + BN) * 64;    // elements per stage: X rows, then W rows
   constexpr int LA = STAGES - 1;           // slices in flight beyond the current one
   static_assert(STAGES >= 2 && STAGES <= 4, "the vmcnt cases below cover 1 to 3 slices");
@@ -210,7 +219,7 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int nbn = (g.N + BN - 1) / BN;
   const int ntile = ((g.M + BM - 1) / BM) * nbn;
   const int xcd = blockIdx.x & 7, q = ntile >> 3, r = ntile & 7;
@@ -400,11 +409,11 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
     }
   __syncthreads();
   constexpr int CPR = BN / 8;  // 16-byte pieces per tile row
-  static_assert(BM * CPR % 256 == 0, "row pieces split evenly over the threads");
+  static_assert(BM * CPR % NT == 0, "row pieces split evenly over the threads");
   if constexpr (!QKV) {
 #pragma unroll
-    for (int it = 0; it < BM * CPR / 256; ++it) {
-      const int idx = tid + 256 * it;
+    for (int it = 0; it < BM * CPR / NT; ++it) {
+      const int idx = tid + NT * it;
       const int rrow = idx / CPR, c = idx % CPR;
       const int m = m0 + rrow, n = n0 + c * 8;
       if (m < g.M && n < g.N)
@@ -414,8 +423,8 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   } else if (which < 2) {
     // Q rows to q_out, K rows into the ring slot of the token's frame
 #pragma unroll
-    for (int it = 0; it < BM * CPR / 256; ++it) {
-      const int idx = tid + 256 * it;
+    for (int it = 0; it < BM * CPR / NT; ++it) {
+      const int idx = tid + NT * it;
       const int rrow = idx / CPR, c = idx % CPR;
       const int m = m0 + rrow;
       if (m < g.M) {
@@ -435,10 +444,10 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
     // The tokens of a piece share a frame (the tile starts at a multiple of
     // 8 and T is a multiple of 8).
     constexpr int TG = BM / 8;   // token groups per tile, a multiple of 8
-    static_assert(TG % 8 == 0 && BN * TG % 256 == 0, "token groups in blocks of 8");
+    static_assert(TG % 8 == 0 && BN * TG % NT == 0, "token groups in blocks of 8");
 #pragma unroll
-    for (int it = 0; it < BN * TG / 256; ++it) {
-      const int idx = tid + 256 * it;
+    for (int it = 0; it < BN * TG / NT; ++it) {
+      const int idx = tid + NT * it;
       const int tg = (idx / (8 * BN)) * 8 + idx % 8;
       const int d = (idx / 8) % BN;
       const int m = m0 + tg * 8;
@@ -465,10 +474,10 @@ hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_
   // one head per output tile: the tile's feature width is the head size
   if (e.D == 128) {
     dim3 grid(((g.M + 255) / 256) * (g.N / 128));
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, true>), grid, dim3(256), 0, s, g, e);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, true, 4, 2>), grid, dim3(512), 0, s, g, e);
   } else {
     dim3 grid(((g.M + 191) / 192) * (g.N / 64));
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, true>), grid, dim3(256), 0, s, g, e);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, true, 2, 2>), grid, dim3(256), 0, s, g, e);
   }
   return hipGetLastError();
 }
@@ -476,15 +485,18 @@ hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_
 hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s) {
   if (g.K % 64 == 0 && int64_t(g.M) * g.K < (int64_t(1) << 31) &&
       int64_t(g.N) * g.K < (int64_t(1) << 31)) {
-    // narrow outputs (the rank-r factor product) get 192 x 64 tiles, wide
-    // ones 256 x 128: at 4680 rows either grid is one round on 256 CUs
+    // narrow outputs (the rank-r factor product) get 128 x 128 tiles (148
+    // workgroups at 4680 x 512), wide ones 256 x 128 (228 at 4680 x 1536):
+    // one round on 256 CUs, 8 waves each
     const QkvEpilogue none{};
     if (g.N <= 768) {
-      dim3 grid(((g.M + 191) / 192) * ((g.N + 63) / 64));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, false>), grid, dim3(256), 0, s, g, none);
+      dim3 grid(((g.M + 127) / 128) * ((g.N + 127) / 128));
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<128, 128, 3, false, 4, 2>), grid, dim3(512), 0, s, g,
+                         none);
     } else {
       dim3 grid(((g.M + 255) / 256) * ((g.N + 127) / 128));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, false>), grid, dim3(256), 0, s, g, none);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, false, 4, 2>), grid, dim3(512), 0, s, g,
+                         none);
     }
     return hipGetLastError();
   }
