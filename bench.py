@@ -45,7 +45,7 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # whenever the attention kernels change (absent = not measured for the
 # current kernels).
 ATTN_TRAFFIC_BYTES = {
-    ("wan_window", "whole"): (2 * 109091 + 17699) * 1024,
+    ("wan_window", "whole"): (2 * 109102 + 17700) * 1024,
     ("wan_720p", "split"): (2 * (590041 + 17004) + 62659 + 204) * 1024,   # attention + merge
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
