@@ -46,7 +46,7 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # current kernels).
 ATTN_TRAFFIC_BYTES = {
     ("wan_window", "whole"): (2 * 109102 + 17700) * 1024,
-    ("wan_720p", "split"): (2 * (590041 + 17004) + 62659 + 204) * 1024,   # attention + merge
+    ("wan_720p", "split"): (2 * (590332 + 17004) + 62667 + 204) * 1024,   # attention + merge
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
