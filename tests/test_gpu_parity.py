@@ -163,8 +163,8 @@ def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True, n_wg=None):
     return P.from_device_bf16(out), (l.cpu().numpy() if lse else None)
 
 
-def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None):
-    w = wl.ALL[name]
+def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None, w=None):
+    w = wl.ALL[name] if w is None else w
     for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
         qb = wl.chunk_tokens(w, wl.TAG_Q, c)
         rows = np.arange(w.n_q) if (c in full_chunks or w.n_q <= 512) else \
@@ -211,6 +211,18 @@ def test_window_attn_split_full_compare(name, n_wg):
 
 def test_window_attn_split_wan_window():
     _attn_case("wan_window", full_chunks=(5,), n_wg=0)
+
+
+# Head size 64 at full size: the Wan frame grid and window with 24 heads of
+# 64 (hidden 1536), so the D = 64 tiles straddle 1560-token frames over a
+# 12-frame window, on sampled rows of every chunk, both schedules.
+WAN_WINDOW_D64 = wl.WAN_WINDOW.replace(name="wan_window_d64", n_heads=24, head_dim=64,
+                                       pairs=(12, 10, 10))
+
+
+@pytest.mark.parametrize("n_wg", [None, 0])
+def test_window_attn_d64_wan_grid(n_wg):
+    _attn_case("wan_window_d64", n_wg=n_wg, rows_per_chunk=160, w=WAN_WINDOW_D64)
 
 
 def test_window_attn_split_wan_720p():
