@@ -711,6 +711,12 @@ def test_qkv_append_wan_window():
     _qkv_case(w, chunks_checked=(0, 5), rows=_sample_rows(w.n_q, 160, seed=3))
 
 
+def test_qkv_append_d64_wan_grid():
+    # the 64-wide-head tile (192 x 64, 4 waves) on the Wan grid: 24 heads
+    w = WAN_WINDOW_D64
+    _qkv_case(w, chunks_checked=(0, 5), rows=_sample_rows(w.n_q, 160, seed=4))
+
+
 def test_densified_rank_1413_projection():
     """The pages' rank, 0.92 x 1536 = 1413, is above the 768 break-even, so the
     value projection runs dense with W_r = A_r B_r re-densified on the GPU
