@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -23,6 +24,8 @@ ARCH = "gfx950"
 
 SOURCES = ["ust_host.cpp", "rope_table.hip", "kv_append.hip", "window_attn.hip", "sampler.hip",
            "gemm.hip"]
+# sources whose inline-asm global->LDS loads take a scalar base address
+DMA_SOURCES = ["window_attn.hip", "gemm.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
@@ -57,11 +60,77 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _sgpr_set(tok: str) -> set:
+    m = re.fullmatch(r"s(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def check_dma_base_hazards(asm: str) -> list:
+    """Scan gfx950 assembly for inline-asm `global_load_lds_dwordx4 vN, s[a:b]`
+    whose scalar base was written by a vector instruction fewer than 5 wait
+    states earlier.  The hardware does not interlock a VALU write of an SGPR
+    with a vector-memory read of it (the CDNA3/CDNA4 ISA guides list 5 wait
+    states), and the compiler inserts none before inline asm, so such a load
+    can use a stale address.  A look-back that meets a label before 5 wait
+    states is reported too (another predecessor could hold the write).
+    Returns one message per offending load."""
+    lines = asm.split("\n")
+    found = []
+    for i, line in enumerate(lines):
+        m = re.match(r"\s*global_load_lds_dwordx4 v\d+, (s\[\d+:\d+\])", line)
+        if not m:
+            continue
+        base = _sgpr_set(m.group(1))
+        ws, j = 0, i - 1
+        while j >= 0 and ws < 5:
+            t = lines[j].strip()
+            j -= 1
+            if re.match(r"\.LBB\d+_\d+:", t) or re.match(r"[A-Za-z_][\w.$]*:", t):
+                found.append(f"line {i + 1}: block boundary {t} {ws} wait states before")
+                break
+            if not t or t.startswith(";") or t.startswith("."):
+                continue
+            op = t.split()[0]
+            if op == "s_nop":
+                ws += int(t.split()[1], 0) + 1
+                continue
+            if op.startswith("v_") and len(t.split()) > 1 and _sgpr_set(t.split()[1].rstrip(",")) & base:
+                found.append(f"line {i + 1}: base {m.group(1)} written by '{t}' {ws} wait states before")
+                break
+            ws += 1
+    return found
+
+
+def _check_dma_source(src: str, verbose: bool) -> None:
+    path = os.path.join(CSRC, src)
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".s")
+    cmd = [hipcc()] + COMMON + DEVICE + ["--cuda-device-only", "-S", path, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"assembling {src} failed:\n{r.stderr}")
+    bad = check_dma_base_hazards(open(out).read())
+    if bad:
+        raise RuntimeError(f"{src}: scalar base of a global->LDS load written by a vector "
+                           f"instruction without the 5 wait states:\n" + "\n".join(bad[:20]))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile and link libust.so; returns its path."""
+    """Compile and link libust.so; returns its path.  The device assembly of
+    the sources with global->LDS loads is checked for a vector-written
+    scalar base (check_dma_base_hazards)."""
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(DMA_SOURCES))) as ex:
+        checks = [ex.submit(_check_dma_source, s, verbose) for s in DMA_SOURCES]
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        for c in checks:
+            c.result()
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
