@@ -76,33 +76,63 @@ def check_dma_base_hazards(asm: str) -> list:
     states earlier.  The hardware does not interlock a VALU write of an SGPR
     with a vector-memory read of it (the CDNA3/CDNA4 ISA guides list 5 wait
     states), and the compiler inserts none before inline asm, so such a load
-    can use a stale address.  A look-back that meets a label before 5 wait
-    states is reported too (another predecessor could hold the write).
-    Returns one message per offending load."""
-    lines = asm.split("\n")
+    can use a stale address.  The look-back follows every path into a block
+    (branches to its label and the fall-through) and every instruction
+    counts one wait state (s_nop N counts N + 1).  Returns one message per
+    offending load and path."""
+    lines = [l.strip() for l in asm.split("\n")]
+    label_at = {}
+    preds = {}
+    for i, t in enumerate(lines):
+        m = re.match(r"(\.LBB\d+_\d+):", t)
+        if m:
+            label_at[m.group(1)] = i
+        m = re.match(r"s_c?branch\w* (\.LBB\d+_\d+)", t)
+        if m:
+            preds.setdefault(m.group(1), []).append(i)
+
+    def is_insn(t: str) -> bool:
+        return bool(t) and not t.startswith(";") and not t.startswith(".") and not t.endswith(":")
+
     found = []
-    for i, line in enumerate(lines):
-        m = re.match(r"\s*global_load_lds_dwordx4 v\d+, (s\[\d+:\d+\])", line)
-        if not m:
-            continue
-        base = _sgpr_set(m.group(1))
-        ws, j = 0, i - 1
+
+    def walk(j: int, ws: int, base: set, load_line: int, seen: set) -> None:
         while j >= 0 and ws < 5:
-            t = lines[j].strip()
+            t = lines[j]
+            m = re.match(r"(\.LBB\d+_\d+):", t)
+            if m:
+                # every path into the block: branches to it and the fall-through
+                for src in preds.get(m.group(1), []):
+                    if (src, ws) not in seen:
+                        seen.add((src, ws))
+                        walk(src, ws, base, load_line, seen)
+                k = j - 1
+                while k >= 0 and not is_insn(lines[k]) and not re.match(r"\.LBB\d+_\d+:", lines[k]) \
+                        and not re.match(r"[A-Za-z_][\w.$]*:", lines[k]):
+                    k -= 1
+                if k >= 0 and is_insn(lines[k]) and lines[k].split()[0] in ("s_branch", "s_endpgm", "s_setpc_b64"):
+                    return
+                j -= 1
+                continue
+            if re.match(r"[A-Za-z_][\w.$]*:", t):
+                return   # function entry: nothing precedes
             j -= 1
-            if re.match(r"\.LBB\d+_\d+:", t) or re.match(r"[A-Za-z_][\w.$]*:", t):
-                found.append(f"line {i + 1}: block boundary {t} {ws} wait states before")
-                break
-            if not t or t.startswith(";") or t.startswith("."):
+            if not is_insn(t):
                 continue
             op = t.split()[0]
             if op == "s_nop":
                 ws += int(t.split()[1], 0) + 1
                 continue
             if op.startswith("v_") and len(t.split()) > 1 and _sgpr_set(t.split()[1].rstrip(",")) & base:
-                found.append(f"line {i + 1}: base {m.group(1)} written by '{t}' {ws} wait states before")
-                break
+                found.append(f"line {load_line + 1}: base written by '{t}' (line {j + 2}) "
+                             f"{ws} wait states before")
+                return
             ws += 1
+
+    for i, t in enumerate(lines):
+        m = re.match(r"global_load_lds_dwordx4 v\d+, (s\[\d+:\d+\])", t)
+        if m:
+            walk(i - 1, 0, _sgpr_set(m.group(1)), i, set())
     return found
 
 

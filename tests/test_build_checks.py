@@ -36,9 +36,25 @@ def test_scalar_written_base_and_enough_wait_states_pass():
         assert check_dma_base_hazards(asm) == []
 
 
-def test_too_few_wait_states_and_block_boundaries_are_flagged():
+def test_too_few_wait_states_are_flagged_on_every_path_into_a_block():
     short = "\tv_readlane_b32 s9, v253, 3\n\ts_nop 2\n\tglobal_load_lds_dwordx4 v1, s[8:9]\n"
     assert len(check_dma_base_hazards(short)) == 1
-    # another predecessor of the block could hold the write
-    label = "\ts_mov_b32 s4, 0\n.LBB0_7:\n\tglobal_load_lds_dwordx4 v1, s[4:5]\n"
-    assert len(check_dma_base_hazards(label)) == 1
+    # the write reaches the load through a taken branch
+    branch = """
+\tv_readfirstlane_b32 s4, v1
+\ts_cbranch_scc1 .LBB0_7
+\ts_mov_b32 s20, 0
+\ts_branch .LBB0_8
+.LBB0_7:
+\tglobal_load_lds_dwordx4 v1, s[4:5]
+.LBB0_8:
+\ts_endpgm
+"""
+    assert len(check_dma_base_hazards(branch)) == 1
+    # ... and through a fall-through into the load's block
+    fall = "\tv_readfirstlane_b32 s5, v1\n.LBB0_9:\n\tglobal_load_lds_dwordx4 v1, s[4:5]\n"
+    assert len(check_dma_base_hazards(fall)) == 1
+    # clean on both paths: the branch source wrote the base with a scalar op,
+    # and the block is not entered by falling through
+    clean = branch.replace("v_readfirstlane_b32 s4, v1", "s_mov_b32 s4, s30")
+    assert check_dma_base_hazards(clean) == []
