@@ -87,8 +87,8 @@ def attn_flops(n_q, n_k, d, h):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
-              "multi-GPU runs are not part of it", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); "
+              "the path has no multi-GPU implementation", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
