@@ -41,12 +41,11 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # HBM traffic of one steady-state attention (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE per dispatch on this workload, scaled by the counter-to-byte
 # factors of a 1 GiB device copy in the same run: read = 2 x FETCH_SIZE KiB,
-# written = WRITE_SIZE KiB), per (workload, schedule).  Must be re-measured
-# whenever the attention kernels change (absent = not measured for the
-# current kernels).
-ATTN_TRAFFIC_BYTES = {
-    ("wan_window", "whole"): (2 * 109102 + 17700) * 1024,
-    ("wan_720p", "split"): (2 * (590332 + 17004) + 62667 + 204) * 1024,   # attention + merge
+# written = WRITE_SIZE KiB), per (workload, schedule), with the hash of the
+# attention kernel's sources the counters were taken on.  The line reports
+# the figure only while the sources still hash the same (null otherwise).
+ATTN_SOURCES = ("window_attn.hip", "attn_schedule.h", "ust_device.h")
+ATTN_TRAFFIC = {
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
@@ -77,11 +76,78 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM traffic counters)")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the measured MFMA-rate and copy-rate calibration")
     return ap.parse_args()
 
 
 def attn_flops(n_q, n_k, d, h):
     return 4.0 * n_q * n_k * d * h      # QK^T and PV, 2 flop per multiply-add
+
+
+def attn_source_sha16():
+    """sha256 (first 16 hex digits) of the attention kernel's sources."""
+    import hashlib
+    hs = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "causal_video_diffusion_amd", "csrc", name), "rb") as f:
+            hs.update(f.read())
+    return hs.hexdigest()[:16]
+
+
+def attn_traffic(workload, schedule):
+    """Counter-measured bytes of the attention, if taken on these sources."""
+    t = ATTN_TRAFFIC.get((workload, schedule))
+    return t["bytes"] if t and t["src_sha16"] == attn_source_sha16() else None
+
+
+def pct(xs):
+    """median, p10, p90 of a list of times."""
+    import numpy as np
+    a = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
+
+
+def calibrate(stream):
+    """Rates this GPU sustains, measured in this process before the timed
+    region: the bf16 MFMA rate of a kernel that only issues MFMAs (one
+    workgroup of 8 waves per compute unit, ~10 ms), and a plain 1 GiB device
+    copy (bytes read + written per second)."""
+    import torch
+    from causal_video_diffusion_amd import _binding as B
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    iters = 4000
+    for _ in range(3):
+        B.ust_calib_mfma_bf16(cus, iters, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps, flops = 10, 0.0
+    e0.record(stream)
+    for _ in range(reps):
+        flops += B.ust_calib_mfma_bf16(cus, iters, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_bf16_TFLOPs": round(mfma_tflops, 1), "copy_GBs": round(copy_gbs, 1),
+            "note": f"MFMA-only kernel (ust_calib_mfma_bf16: {cus} workgroups x 8 waves, 4 "
+                    f"independent 32x32x16 bf16 chains per wave, {reps} launches) and a 1 GiB "
+                    f"device copy (read + written bytes), both timed with HIP events in this "
+                    f"process before the timed region"}
 
 
 def main():
@@ -185,6 +251,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    calib = None if args.no_calib else calibrate(stream)
+
     for i in range(max(args.warmup, len(steady))):   # every timed chunk appended once
         step(i)
     torch.cuda.synchronize()
@@ -200,7 +268,10 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    attn_us = 1000.0 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    attn_each = [1000.0 * e[2].elapsed_time(e[3]) for e in evs]
+    attn_us = float(np.mean(attn_each))
+    # one step spans the end of one attention to the end of the next
+    step_each = [evs[i][3].elapsed_time(evs[i + 1][3]) for i in range(args.steps - 1)]
 
     # per-stage split, outside the timed region, with all five events
     sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -221,22 +292,36 @@ def main():
     b1.record(stream)
     torch.cuda.synchronize()
     stage["rope_k_append_batched_us"] = 1000.0 * b0.elapsed_time(b1) / 20
-    # the append from HBM: reading 512 MiB before each rep evicts its inputs
-    # from L2 and the 256 MB MALL (a read leaves no dirty lines behind whose
-    # write-back the append would pay for); events around the append alone
+    # the append from HBM: reading 512 MiB before each append evicts its
+    # inputs from L2 and the 256 MB MALL (a read leaves no dirty lines behind
+    # whose write-back the append would pay for).  No event sits between a
+    # flush and its append: 20 (flush, append) pairs back to back are timed
+    # against 20 flushes alone, and the difference is the 20 cold appends.
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(20):
-        flush.max()
+    fsum = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def flush_read():
+        torch.sum(flush, dtype=torch.int64, out=fsum)
+
+    def timed(with_append):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
+        for _ in range(20):
+            flush_read()
+            if with_append:
+                B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
         e1.record(stream)
         torch.cuda.synchronize()
-        cold.append(1000.0 * e0.elapsed_time(e1))
+        return 1000.0 * e0.elapsed_time(e1)
+
+    timed(True)
+    cold_each = []
+    for _ in range(5):
+        pair_us, flush_us = timed(True), timed(False)
+        cold_each.append((pair_us - flush_us) / 20)
     del flush
-    stage["rope_k_append_cold_us"] = float(np.median(cold))
+    stage["rope_k_append_cold_us"] = float(np.median(cold_each))
     attn_tflops = flops / (attn_us * 1e-6) / 1e12
     append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
     lowrank_flops = 2 * 2.0 * w.n_q * w.hidden * w.rank
@@ -272,17 +357,22 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": ATTN_TRAFFIC_BYTES.get((w.name, schedule)),
+            "traffic": attn_traffic(w.name, schedule),
             "kernel": ("window_attn_kernel<128> + window_attn_combine_kernel (one span)" if split
                        else "window_attn_kernel<128>"),
             "kernel_us": round(attn_us, 2),
+            "kernel_us_spread": pct(attn_each),
+            "attn_src_sha16": attn_source_sha16(),
         },
+        "ms_per_step_spread": pct(step_each),
         "stages_us": {k: round(v, 2) for k, v in stage.items()},
         "stages_note": "separate untimed pass with an event between every stage "
                        "(each event adds ~2-3 us; stage times include launch gaps); "
                        "rope_k_append_batched_us: 20 appends back to back, per launch "
-                       "(no event overhead; inputs warm); rope_k_append_cold_us: the append "
-                       "alone after reading 512 MiB, median of 20 (event overhead included)",
+                       "(no event overhead; inputs warm); rope_k_append_cold_us: 20 "
+                       "(512 MiB read, append) pairs minus 20 reads alone, per append, "
+                       "median of 5 (no event between a read and its append); the 60% "
+                       "HBM target is compared with this cold figure",
         "stages": {
             "rope_k_append_GBs": round(append_bytes / (stage["rope_k_append_us"] * 1e-6) / 1e9, 1),
             "rope_k_append_hbm_frac": round(append_bytes / (stage["rope_k_append_us"] * 1e-6)
@@ -294,7 +384,18 @@ def main():
             "lowrank_v_o_TFLOPs": round(lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"])
                                                          * 1e-6) / 1e12, 1),
         },
+        "targets": {
+            "attention_frac_of_bf16_peak": {"target": 0.5, "got": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
+            "rope_k_append_cold_hbm_frac": {"target": 0.6, "got": round(
+                append_bytes / (stage["rope_k_append_cold_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        },
     }
+    if calib is not None:
+        result["calibration"] = calib
+        result["roofline"]["measured_peak"] = calib["mfma_bf16_TFLOPs"]
+        result["roofline"]["frac_of_measured_peak"] = round(attn_tflops / calib["mfma_bf16_TFLOPs"], 4)
+        result["stages"]["rope_k_append_cold_frac_of_measured_copy"] = round(
+            append_bytes / (stage["rope_k_append_cold_us"] * 1e-6) / 1e9 / calib["copy_GBs"], 4)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, C, args.cpu_reps)

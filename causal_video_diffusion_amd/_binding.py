@@ -22,7 +22,8 @@ STATUS = {0: "UST_OK", 1: "UST_E_NULL", 2: "UST_E_SHAPE", 3: "UST_E_RANGE",
 EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
            "ust_window_attn", "ust_window_attn_work_bytes", "ust_window_attn_split",
            "ust_qkv_append", "ust_lowrank_proj", "ust_flow_step", "ust_slot_of_frame",
-           "ust_window_plan", "ust_sigma_schedule", "ust_status_str", "ust_last_error")
+           "ust_window_plan", "ust_sigma_schedule", "ust_status_str", "ust_last_error",
+           "ust_calib_mfma_bf16")
 
 
 class UstError(RuntimeError):
@@ -75,6 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(F64)]),
         "ust_slot_of_frame": (I32, [KP, I32]),
         "ust_window_plan": (I32, [GP, KP, I32, I32, IP, IP, I32, IP]),
+        "ust_calib_mfma_bf16": (I32, [I32, I32, P, ctypes.POINTER(F64), P]),
         "ust_status_str": (ctypes.c_char_p, [I32]),
         "ust_last_error": (ctypes.c_char_p, []),
     }
@@ -207,3 +209,11 @@ def ust_window_plan(g: Geom, ring: Kv, frame_start: int, n_recent: int,
     _check(load().ust_window_plan(ctypes.byref(g), ctypes.byref(ring), frame_start,
                                   n_recent, frames, slots, cap, ctypes.byref(n)))
     return list(frames[:n.value]), list(slots[:n.value])
+
+
+def ust_calib_mfma_bf16(n_workgroups: int, iters: int, out, stream=None) -> float:
+    """Launch the MFMA-only measurement kernel; returns its flop count."""
+    flops = ctypes.c_double(0.0)
+    _check(load().ust_calib_mfma_bf16(n_workgroups, iters, _ptr(out), ctypes.byref(flops),
+                                      _stream(stream)))
+    return flops.value

@@ -5,6 +5,7 @@
 // a thread-local error text, and never lets a C++ exception escape.
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -100,30 +101,43 @@ ust_status chunk_slots(const ust_geom* g, const ust_kv* kv, int32_t n_tab_frames
   return UST_OK;
 }
 
-// The window plan (see ust_window_plan in ust.h).
+// The window plan (see ust_window_plan in ust.h).  Only the frames that can
+// be in the window are visited: the sinks before the chunk, then from the
+// first recent frame (or the first non-sink frame) to the chunk's last frame.
 ust_status plan(const ust_geom* g, const ust_kv* kv, int32_t frame_start, int32_t n_recent,
                 int32_t* frames, int32_t* slots, int32_t cap, int32_t* n_out) {
   if (frame_start < 0) return fail(UST_E_RANGE, "frame_start %d < 0", frame_start);
   if (n_recent < -1) return fail(UST_E_RANGE, "n_recent %d < -1", n_recent);
-  const int32_t last = frame_start + g->chunk_frames - 1;  // newest frame written
-  const int32_t ring = kv->n_slots - kv->n_sink;
+  const int64_t last = int64_t(frame_start) + g->chunk_frames - 1;  // newest frame written
+  if (last > INT32_MAX)
+    return fail(UST_E_RANGE, "chunk at frame %d runs past frame %d", frame_start, INT32_MAX);
+  const int64_t ring = int64_t(kv->n_slots) - kv->n_sink;
   int32_t n = 0;
-  for (int32_t f = 0; f <= last; ++f) {
-    const bool current = f >= frame_start;
-    const bool sink = f < kv->n_sink;
-    const bool recent = n_recent < 0 || f >= frame_start - n_recent;
-    if (!(current || sink || recent)) continue;
+  auto take = [&](int64_t f, bool sink) -> ust_status {
     // a ring frame f is overwritten once frame f + ring has been written
-    if (!sink && int64_t(f) + ring <= last)
+    if (!sink && f + ring <= last)
       return fail(UST_E_RANGE,
-                  "window frame %d is no longer in the ring (%d slots, %d sinks) after frame %d",
-                  f, kv->n_slots, kv->n_sink, last);
+                  "window frame %lld is no longer in the ring (%d slots, %d sinks) after frame %lld",
+                  static_cast<long long>(f), kv->n_slots, kv->n_sink, static_cast<long long>(last));
     if (n >= UST_MAX_WINDOW_FRAMES)
       return fail(UST_E_RANGE, "window exceeds %d frames", UST_MAX_WINDOW_FRAMES);
     if (n >= cap) return fail(UST_E_SHAPE, "plan capacity %d too small", cap);
-    frames[n] = f;
-    slots[n] = slot_of(f, kv->n_slots, kv->n_sink);
+    frames[n] = int32_t(f);
+    slots[n] = slot_of(int32_t(f), kv->n_slots, kv->n_sink);
     ++n;
+    return UST_OK;
+  };
+  // sink frames before the chunk (a sink inside the chunk counts as current)
+  const int64_t sink_end = std::min<int64_t>(kv->n_sink, frame_start);
+  for (int64_t f = 0; f < sink_end; ++f) {
+    const ust_status s = take(f, true);
+    if (s != UST_OK) return s;
+  }
+  // recent frames (every prior frame when n_recent = -1), then the chunk
+  const int64_t recent0 = n_recent < 0 ? 0 : std::max<int64_t>(0, int64_t(frame_start) - n_recent);
+  for (int64_t f = std::max(sink_end, recent0); f <= last; ++f) {
+    const ust_status s = take(f, f < kv->n_sink);
+    if (s != UST_OK) return s;
   }
   *n_out = n;
   return UST_OK;
@@ -477,6 +491,20 @@ ust_status ust_flow_step(const float* x, const void* v, const float* noise, floa
     ust::FlowStepArgs a{x, static_cast<const uint16_t*>(v), sigma_next != 0.f ? noise : nullptr,
                         x0_out, x_next, n, sigma, sigma_next, 1.0f - sigma_next};
     return hip_status(ust::launch_flow_step(a, stream), "flow_step launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_calib_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out,
+                               double* flops_out, hipStream_t stream) {
+  try {
+    if (!out) return fail(UST_E_NULL, "out is NULL");
+    if (n_workgroups <= 0 || n_workgroups > 65536 || iters <= 0)
+      return fail(UST_E_SHAPE, "n_workgroups %d / iters %d out of range", n_workgroups, iters);
+    if (!aligned16(out)) return fail(UST_E_ALIGN, "out must be 16-byte aligned");
+    if (flops_out) *flops_out = ust::calib_mfma_flops(n_workgroups, iters);
+    return hip_status(ust::launch_calib_mfma(n_workgroups, iters, out, stream), "calib launch");
   } catch (...) {
     return fail(UST_E_HIP, "internal error");
   }

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/ust.h"
+#include "../../include/ust_calib.h"
 
 namespace ust {
 
@@ -97,5 +98,8 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 // workspace bytes of the key-split schedule over n_wg workgroups
 size_t window_attn_work_bytes(int32_t head_dim, int32_t n_wg);
 hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
+// measurement aid (calib.hip): MFMA-only kernel and its flop count
+hipError_t launch_calib_mfma(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
+double calib_mfma_flops(int32_t n_wg, int32_t iters);
 
 }  // namespace ust

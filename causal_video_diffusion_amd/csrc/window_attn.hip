@@ -416,7 +416,8 @@ window_attn_kernel(AttnArgs a) {
       // when the tile's sum leaves [0, kSumBound]: a probability so large it
       // could overflow, an infinity or a NaN.  The scores are kept until that
       // test, so the rare path rescales and redoes the tile.
-      auto rescale = [&](bool first) __attribute__((always_inline)) {
+      auto rescale = [&](auto first_tag) __attribute__((always_inline)) {
+        constexpr bool first = decltype(first_tag)::value;
         float m4[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -427,13 +428,19 @@ window_attn_kernel(AttnArgs a) {
         }
         const float tmax = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
         const float shift = (first || tmax > kRescale) ? tmax : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-shift);
         mref += shift;
-        lrow *= alpha;
+        if constexpr (!first) {
+          // On a segment's first tile the running sum and the output are
+          // still zero and are not scaled: alpha = 2^-tmax overflows to
+          // infinity when the whole tile scores below -128 (log2 units), and
+          // 0 * inf would be NaN.
+          const float alpha = __builtin_amdgcn_exp2f(-shift);
+          lrow *= alpha;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+          for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+            for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -468,10 +475,10 @@ window_attn_kernel(AttnArgs a) {
           }
         return (ls[0] + ls[1]) + (ls[2] + ls[3]);
       };
-      if (j == 0) rescale(true);
+      if (j == 0) rescale(std::true_type{});
       float lnew = lrow + probs();
       if (__builtin_amdgcn_ballot_w64(!(lnew <= kSumBound))) {
-        rescale(false);
+        rescale(std::false_type{});
         lnew = lrow + probs();
       }
       lrow = lnew;

@@ -163,10 +163,19 @@ def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True, n_wg=None):
     return P.from_device_bf16(out), (l.cpu().numpy() if lse else None)
 
 
-def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None, w=None):
+def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None, w=None, chunks=None,
+               q_mult=1.0):
+    """Attention of every chunk (or of `chunks`) after its append, against the
+    oracle on all rows of small chunks and of `full_chunks`, on sampled rows
+    otherwise.  q_mult scales the queries (a power of two keeps them exact in
+    bf16) to make the softmax peaky."""
     w = wl.ALL[name] if w is None else w
     for c, g, table, ring, cache, (cos, sin), kb, vb in _append_all(w):
+        if chunks is not None and c not in chunks:
+            continue
         qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        if q_mult != 1.0:
+            qb = wl.f32_to_bf16_bits((_f64(qb) * q_mult).astype(np.float32))
         rows = np.arange(w.n_q) if (c in full_chunks or w.n_q <= 512) else \
             _sample_rows(w.n_q, rows_per_chunk, seed=c)
         mode = "" if n_wg is None else f" split over {n_wg or 'all CUs'}"
@@ -175,8 +184,14 @@ def _attn_case(name, full_chunks=(), rows_per_chunk=192, n_wg=None, w=None):
         o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c, 3, w.grid_h,
                                        w.grid_w, w.n_slots, w.n_sink, w.n_recent,
                                        rows=rows)
-        assert_close(_f64(o_gpu[rows]), o_ref, f"{name} chunk {c} O")
-        assert_close(lse_gpu[:, rows], lse_ref, f"{name} chunk {c} lse", max_abs=2e-2,
+        # The bar's absolute part is for outputs of unit scale (the workloads'
+        # outputs stay well below 1).  Peaky queries give outputs up to ~3.4,
+        # where one bf16 ulp is 2^-6 and the bf16 rounding of each rotated
+        # query element (2^-9 relative) moves scores of ~15 by ~0.03: the
+        # absolute part then scales with the largest output.
+        o_scale = max(1.0, float(np.max(np.abs(o_ref)))) if q_mult != 1.0 else 1.0
+        assert_close(_f64(o_gpu[rows]), o_ref, f"{name} chunk {c} O", max_abs=MAX_ABS * o_scale)
+        assert_close(lse_gpu[:, rows], lse_ref, f"{name} chunk {c} lse", max_abs=2e-2 * q_mult,
                      rel_l2=1e-3)
 
 
@@ -190,8 +205,18 @@ def test_window_attn_wan_window():
     _attn_case("wan_window", full_chunks=(5,))
 
 
+def test_window_attn_wan_window_peaky():
+    # queries x4: scores four times wider, so the softmax is far from uniform
+    # (a stress input beside the random-weight workload); chunk 5 in full.
+    # A CPU model of the kernel's roundings (bf16 rotated query, bf16 cached
+    # key, bf16 probabilities, bf16 output) puts max-abs near 3e-2 here, at
+    # outputs up to 3.4: the absolute bar is scaled by the largest output
+    _attn_case("wan_window", full_chunks=(5,), chunks=(5,), q_mult=4.0)
+
+
 def test_window_attn_wan_full_cache():
-    _attn_case("wan_full")
+    # the last chunk (32760 keys, every prior frame) in full, the others sampled
+    _attn_case("wan_full", full_chunks=(6,))
 
 
 def test_window_attn_wan_720p():
@@ -400,6 +425,91 @@ def test_window_attn_scores_far_above_the_first_tile():
             print(f"  lse: max err {err.max():.3e}, max err / bound {(err / bound).max():.3f}",
                   flush=True)
             assert np.all(err <= bound + 1e-4 * (1 + np.abs(lse_ref))), f"chunk {c} lse"
+
+
+# Dimensions 38..43 are the frame-axis pairs 19..21 (of 22 at head size 128),
+# whose frequencies are at most 10^4^(-19/22) ~ 3.5e-4 rad per frame: the
+# RoPE of a vector living there depends on the frame only, and turns it by
+# less than 0.007 rad over the table (so its cosine part rounds to the same
+# bf16 value in every frame).
+_BIG = slice(38, 44)
+
+
+def _with_big_part(bits, coef):
+    """Zero dimensions 38..43 and put `coef` in their even elements (the first
+    element of each of those three rotation pairs)."""
+    x = _f64(bits).copy()
+    x[..., _BIG] = 0.0
+    x[..., _BIG.start:_BIG.stop:2] = coef
+    return wl.f32_to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("where,offset", [("current", 20.0), ("current", 48.0),
+                                          ("current", 100.0), ("recent", 48.0),
+                                          ("recent", 100.0), ("sink", -100.0)])
+def test_window_attn_rescale_path_random_values(where, offset):
+    """The lazy-rescale path against the oracle element by element, with
+    distinct random value rows.  Every query carries gamma = 16 on the three
+    frame-axis pairs 19..21, and the keys of one chunk carry beta there
+    (others 0), so that chunk's keys score `offset` (natural units) above
+    the rest, and all keys of a frame get the same offset to fp32 rounding:
+    their frame-axis RoPE is the same, and the bf16 rounding of a query's
+    large part shifts them all alike.  Inside the chunk the weights follow
+    the random parts, as accurate as in the plain workload.
+      current, 20: probabilities up to 2^29 against the first tile's
+        reference; no rescale;
+      current / recent, 48: running sums past 2^64: a rescale with finite
+        values, the tile redone (recent: mid-window, later tiles fall far
+        below the new reference);
+      current / recent, 100: exp2 overflows to infinity: the rescale from
+        the raw scores;
+      sink, -100: the window's first tile (the sink frames) scores ~144
+        below every later key (log2 units), so its reference is ~144 below
+        the scores that follow.
+    Chunk 5 of the mid workload (window: sinks 0-2, recent 9-14, current
+    15-17), on both schedules (the split one over 5, 37 and all
+    workgroups, so segments also start inside the offset chunk).  The
+    log-sum-exp carries the bf16 rounding of the queries' large part, so
+    it is held to that bound, per row."""
+    w = wl.MID
+    c_att = 5
+    big_chunk = {"current": 5, "recent": 3, "sink": 0}[where]
+    gamma = 16.0
+    scale = 1.0 / math.sqrt(w.head_dim)
+    beta = float(wl.bf16_bits_to_f64(wl.f32_to_bf16_bits(
+        np.array([offset / (3 * gamma * scale)], np.float32)))[0])
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    cos, sin = O.rope_table(w.n_tab_frames, w.grid_h, w.grid_w, w.pairs, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    for c in range(c_att + 1):
+        kb = _with_big_part(wl.chunk_tokens(w, wl.TAG_K, c), beta if c == big_chunk else 0.0)
+        vb = wl.chunk_tokens(w, wl.TAG_V, c)
+        B.ust_kv_append(g, ring.abi, P.to_device_bf16(kb), P.to_device_bf16(vb),
+                        table.cos, table.sin, w.n_tab_frames, 3 * c)
+        O.kv_append(cache, _f64(kb), _f64(vb), cos, sin, 3 * c, 3, w.grid_h,
+                    w.grid_w, w.n_slots, w.n_sink)
+    qb = _with_big_part(wl.chunk_tokens(w, wl.TAG_Q, c_att), gamma)
+    o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, 3 * c_att, 3, w.grid_h,
+                                   w.grid_w, w.n_slots, w.n_sink, w.n_recent)
+    # lse bound: each rotated, scaled query element is rounded to bf16
+    # (relative error <= 2^-9), so a score moves by at most
+    # 2^-9 scale sum_d |q'_d k_d|; 2^-8 and 1% cover the fp32 rotation
+    f, y, x = O.chunk_positions(3 * c_att, 3, w.grid_h, w.grid_w)
+    qr = np.abs(O.rope_apply(_f64(qb), cos[f, y, x][:, None, :], sin[f, y, x][:, None, :]))
+    _, slots = O.window_slots(3 * c_att, 3, w.n_sink, w.n_recent, w.n_slots)
+    bound = np.empty((w.n_heads, w.n_q))
+    for h in range(w.n_heads):
+        kabs = np.abs(cache.k[slots][:, h].reshape(-1, w.head_dim))
+        bound[h] = 1.01 * 2.0 ** -8 * scale * (qr[:, h] @ kabs.T).max(axis=1)
+    for n_wg in (None, 0, 5, 37):
+        print(f"[rescale path: {where} chunk offset {offset:+g}, n_wg {n_wg}]", flush=True)
+        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c_att, n_wg=n_wg)
+        assert_close(_f64(o_gpu), o_ref, f"rescale {where} {offset:+g} n_wg {n_wg} O")
+        err = np.abs(lse_gpu - lse_ref)
+        assert np.all(err <= bound + 1e-4 * (1 + np.abs(lse_ref))), \
+            f"lse: max err {err.max():.3e}, max err / bound {(err / bound).max():.3f}"
 
 
 def test_v_one_gives_one_and_k_zero_gives_mean():

@@ -28,14 +28,19 @@ def lib():
 
 
 def _header_symbols():
-    txt = open(os.path.join(ROOT, "include", "ust.h")).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(ust_[a-z0-9_]+)\s*\(", txt)))
+    """Functions declared by every header under include/."""
+    syms = set()
+    inc = os.path.join(ROOT, "include")
+    for name in sorted(os.listdir(inc)):
+        if name.endswith(".h"):
+            txt = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, name)).read(), flags=re.S)
+            syms |= set(re.findall(r"\b(ust_[a-z0-9_]+)\s*\(", txt))
+    return sorted(syms)
 
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 14
+    assert len(syms) == 15
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -124,6 +129,29 @@ def test_window_plan_errors(lib):
     assert frames == [0, 1] + list(range(3, 129))
     with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
         B.ust_window_plan(g, B.Kv(None, None, 131, 2), 127, 124)
+
+
+def test_window_plan_far_frames(lib):
+    """Frames near the top of the 32-bit range: a chunk whose last frame
+    would pass 2^31 - 1 is rejected (no overflow), and a window far along a
+    stream is planned by visiting only its own frames (this returns at once;
+    a walk from frame 0 would take 2^31 steps)."""
+    g = _geom(wl.WAN_WINDOW)
+    ring = B.Kv(None, None, 21, 3)
+    top = 2 ** 31 - 1
+    for f0 in (top, top - 1):
+        with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+            B.ust_window_plan(g, ring, f0, 6)
+    f0 = top - 2                       # the chunk's last frame is exactly 2^31 - 1
+    frames, slots = B.ust_window_plan(g, ring, f0, 6)
+    assert frames == [0, 1, 2] + list(range(f0 - 6, f0 + 3))
+    assert slots == [O.slot_of_frame(f, 21, 3) for f in frames]
+    # every prior frame: the ring cannot hold them, which is found at once
+    with pytest.raises(cvd.UstError, match="UST_E_RANGE"):
+        B.ust_window_plan(g, ring, f0, -1)
+    # a recent count reaching past frame 0 takes every prior frame once
+    frames, _ = B.ust_window_plan(g, B.Kv(None, None, 400, 3), 30, top)
+    assert frames == list(range(33))
 
 
 def _raw(lib, name, *args):
