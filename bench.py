@@ -46,6 +46,8 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # the figure only while the sources still hash the same (null otherwise).
 ATTN_SOURCES = ("window_attn.hip", "attn_schedule.h", "ust_device.h")
 ATTN_TRAFFIC = {
+    ("wan_window", "whole"): {"src_sha16": "5c8fcf3a7ae9e2c9",
+                              "bytes": (2 * 108170 + 17700) * 1024},
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
@@ -297,11 +299,13 @@ def main():
     # whose write-back the append would pay for).  No event sits between a
     # flush and its append: 20 (flush, append) pairs back to back are timed
     # against 20 flushes alone, and the difference is the 20 cold appends.
-    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-    fsum = torch.empty((), dtype=torch.int64, device="cuda")
+    # (a float32 sum: torch reads the buffer once and writes one value; an
+    # integer sum of bytes would first write a widened copy)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    fsum = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush_read():
-        torch.sum(flush, dtype=torch.int64, out=fsum)
+        torch.sum(flush, dim=0, out=fsum)
 
     def timed(with_append):
         e0 = torch.cuda.Event(enable_timing=True)
