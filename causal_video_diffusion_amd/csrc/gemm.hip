@@ -13,6 +13,7 @@
 //  * When K is a multiple of 64 a pipelined variant (below) streams tiles
 //    straight into LDS instead of through registers.
 
+#include <mutex>
 #include <type_traits>
 
 #include "ust_device.h"
@@ -469,6 +470,31 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
 }
 
 }  // namespace
+
+// Device scratch of ust_lowrank_proj_static: the rank-r intermediate T of one
+// call, for callers that cannot allocate.  Each GPU holds its own copy for
+// the life of the process; kernels get its address from lowrank_scratch(),
+// never from this name (in host code it is a host-side stand-in).
+static __device__ __align__(256) uint16_t scratch[kLowrankScratchElems];
+
+hipError_t lowrank_scratch(uint16_t** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<uint16_t*>(addr[dev]);
+  return hipSuccess;
+}
 
 hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_t s) {
   // one head per output tile: the tile's feature width is the head size

@@ -415,12 +415,18 @@ ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
   }
 }
 
-ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const void* bias,
-                            void* t_work, void* y, int32_t M, int32_t K, int32_t r, int32_t N,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ust_lowrank_proj, and ust_lowrank_proj_static (t_work == nullptr with
+// use_static: the library's device scratch)
+ust_status lowrank_proj(const void* x, const void* a, const void* b, const void* bias,
+                        void* t_work, bool use_static, void* y, int32_t M, int32_t K, int32_t r,
+                        int32_t N, hipStream_t stream) {
   try {
     if (!x || !a || !y) return fail(UST_E_NULL, "x, a or y is NULL");
-    if (b && !t_work) return fail(UST_E_NULL, "t_work is required when b is given");
+    if (b && !t_work && !use_static) return fail(UST_E_NULL, "t_work is required when b is given");
     if (M <= 0 || K <= 0 || r <= 0 || N <= 0)
       return fail(UST_E_SHAPE, "sizes must be positive (M=%d K=%d r=%d N=%d)", M, K, r, N);
     if (!b && N != r) return fail(UST_E_SHAPE, "dense mode (b NULL) needs N == r");
@@ -441,6 +447,13 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const v
       return hip_status(ust::launch_gemm_nt(g1, stream), "lowrank_proj launch");
     }
     uint16_t* t = static_cast<uint16_t*>(t_work);
+    if (use_static) {
+      if (int64_t(M) * r > UST_LOWRANK_STATIC_MAX_ELEMS)
+        return fail(UST_E_RANGE, "M * r = %lld exceeds the static scratch (%d elements)",
+                    static_cast<long long>(int64_t(M) * r), UST_LOWRANK_STATIC_MAX_ELEMS);
+      hipError_t e = ust::lowrank_scratch(&t);
+      if (e != hipSuccess) return hip_status(e, "lowrank_proj_static scratch address");
+    }
     ust::GemmArgs g1{xb, ab, nullptr, t, M, r, K};
     hipError_t e = ust::launch_gemm_nt(g1, stream);
     if (e != hipSuccess) return hip_status(e, "lowrank_proj launch (X A)");
@@ -449,6 +462,22 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const v
   } catch (...) {
     return fail(UST_E_HIP, "internal error");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+ust_status ust_lowrank_proj(const void* x, const void* a, const void* b, const void* bias,
+                            void* t_work, void* y, int32_t M, int32_t K, int32_t r, int32_t N,
+                            hipStream_t stream) {
+  return lowrank_proj(x, a, b, bias, t_work, false, y, M, K, r, N, stream);
+}
+
+ust_status ust_lowrank_proj_static(const void* x, const void* a, const void* b, const void* bias,
+                                   void* y, int32_t M, int32_t K, int32_t r, int32_t N,
+                                   hipStream_t stream) {
+  return lowrank_proj(x, a, b, bias, nullptr, true, y, M, K, r, N, stream);
 }
 
 ust_status ust_sigma_schedule(const int32_t* raw_steps, int32_t n, double shift,

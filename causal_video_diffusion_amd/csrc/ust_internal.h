@@ -98,6 +98,10 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 // workspace bytes of the key-split schedule over n_wg workgroups
 size_t window_attn_work_bytes(int32_t head_dim, int32_t n_wg);
 hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
+// bf16 elements of the device scratch behind ust_lowrank_proj_static
+constexpr size_t kLowrankScratchElems = size_t(UST_LOWRANK_STATIC_MAX_ELEMS);
+// that scratch's address on the current device (looked up once per device)
+hipError_t lowrank_scratch(uint16_t** ptr);
 // measurement aid (calib.hip): MFMA-only kernel and its flop count
 hipError_t launch_calib_mfma(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
 double calib_mfma_flops(int32_t n_wg, int32_t iters);

@@ -22,13 +22,17 @@
  *                         the K/V append fused into the product's epilogue
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
+ *   ust_lowrank_proj_static  the same with the intermediate in a fixed device
+ *                         array, for callers that cannot allocate
  *   ust_flow_step         one step of the chunk sampler: denoised estimate and
  *                         renoising (Table 4; abstract)
  *   ust_sigma_schedule    the sampler's noise levels (host only; Table 4)
  *
  * Conventions (all entry points):
  *  - Device pointers are caller-owned.  The library never allocates, frees
- *    or keeps them past the call.  No entry point allocates device memory.
+ *    or keeps them past the call.  No entry point allocates device memory;
+ *    ust_lowrank_proj_static uses a fixed device array of the library's
+ *    own instead of a caller buffer.
  *  - Every call validates all of its arguments on the host before anything
  *    is launched; on an error nothing is launched, the status says which
  *    class of error, and ust_last_error() (thread-local) gives the detail.
@@ -38,8 +42,9 @@
  *    caller's next synchronisation, not here.
  *  - bf16 is bfloat16 (1-8-7) stored as 16-bit words; fp32 is IEEE binary32.
  *  - Every device pointer must be 16-byte aligned.
- *  - The library holds no mutable global state and is safe to call from
- *    several host threads (each on its own stream).
+ *  - Apart from that array (and the per-device table of its addresses) the
+ *    library holds no mutable global state and is safe to call from several
+ *    host threads (each on its own stream).
  *  - No C++ exception crosses the ABI.
  *
  * Token order: a chunk has chunk_frames * T tokens, T = grid_h * grid_w.
@@ -243,6 +248,26 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b,
                             const void* bias, void* t_work, void* y,
                             int32_t M, int32_t K, int32_t r, int32_t N,
                             hipStream_t stream);
+
+/* Largest M * r that ust_lowrank_proj_static accepts: the bf16 elements of
+ * its device scratch (8 MiB). */
+#define UST_LOWRANK_STATIC_MAX_ELEMS (4 * 1024 * 1024)
+
+/* ust_lowrank_proj without the caller's t_work, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * hosts that forbid allocation): same arguments, result and errors as
+ * ust_lowrank_proj, the same kernels, and T = X A_r kept in a device scratch
+ * array that the library holds, one per GPU, for the life of the process.
+ * The call allocates nothing (its first call on a device looks the array's
+ * address up).  T is written in full before it is read, so nothing carries
+ * over from an earlier call.
+ *   Limit: M * r <= UST_LOWRANK_STATIC_MAX_ELEMS when b != NULL, else
+ *   UST_E_RANGE (b == NULL needs no scratch).
+ *   Calls that overlap on one GPU (different streams, or several host
+ *   threads) share that array and race: order them on one stream. */
+ust_status ust_lowrank_proj_static(const void* x, const void* a, const void* b,
+                                   const void* bias, void* y, int32_t M, int32_t K,
+                                   int32_t r, int32_t N, hipStream_t stream);
 
 /* One step of the chunk sampler (Table 4: the noise levels of the denoising
  * steps and of the clean-cache forward; abstract: the generated frames are

@@ -40,7 +40,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 16
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -173,6 +173,13 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     assert _raw(lib, "ust_rope_table_build", gp, 21, 1e4, None, fake, None)[0] == "UST_E_NULL"
     assert _raw(lib, "ust_lowrank_proj", fake, fake, fake, None, None, fake, 8, 8, 8, 8,
                 None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_lowrank_proj_static", None, fake, fake, None, fake, 8, 8, 8, 8,
+                None)[0] == "UST_E_NULL"
+    # the static scratch holds at most UST_LOWRANK_STATIC_MAX_ELEMS elements of T
+    big_m = B.UST_LOWRANK_STATIC_MAX_ELEMS // 64 + 8
+    st, msg = _raw(lib, "ust_lowrank_proj_static", fake, fake, fake, None, fake, big_m, 64, 64,
+                   64, None)
+    assert st == "UST_E_RANGE" and "static scratch" in msg
     # frames outside the table
     assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 21, 19, None)[0] == "UST_E_RANGE"
     assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake, None,
