@@ -26,5 +26,9 @@ restate its formula; see tests/test_oracle_pins.py):
                               level endpoints of Table 4, recovery of the
                               clean latent from exact velocities, scalar
                               brute force by another algebraic route)
+  conv3d_causal               pinned (scalar brute force, delta kernels that
+                              copy and shift the input in time and space,
+                              causality, torch conv3d in fp64 on explicitly
+                              padded input)
 """
 from .ust_oracle import *  # noqa: F401,F403

@@ -141,3 +141,39 @@ def sample_chunk(dit, x_init: Sequence[float], noises, raw_steps: Sequence[int],
     seen.append(levels[-1])
     labels.append(0.0)
     return [x[k] - levels[-1] * v[k] for k in range(len(x))], seen, labels
+
+
+def conv3d_causal(x, w, bias=None):
+    """Causal 3-D convolution as a scalar quadruple loop over the input
+    positions each output reads (UnStep, abstract: the decoder's convolution
+    kernels; causality and padding are readings): out[t][y][x][o] sums
+    w[o][dt][dy][dx][i] x[t'][y'][x'][i] over t' = t - 2 .. t, y' = y - 1 ..
+    y + 1, x' = x - 1 .. x + 1 inside the input, nested lists in and out."""
+    T, H, W = len(x), len(x[0]), len(x[0][0])
+    Ci, Co = len(x[0][0][0]), len(w)
+    out = []
+    for t in range(T):
+        frame = []
+        for y in range(H):
+            row = []
+            for xx in range(W):
+                vals = []
+                for o in range(Co):
+                    acc = 0.0 if bias is None else float(bias[o])
+                    for tp in range(t - 2, t + 1):
+                        if tp < 0:
+                            continue
+                        for yp in range(y - 1, y + 2):
+                            if yp < 0 or yp >= H:
+                                continue
+                            for xp in range(xx - 1, xx + 2):
+                                if xp < 0 or xp >= W:
+                                    continue
+                                wk = w[o][tp - t + 2][yp - y + 1][xp - xx + 1]
+                                for i in range(Ci):
+                                    acc += wk[i] * x[tp][yp][xp][i]
+                    vals.append(acc)
+                row.append(vals)
+            frame.append(row)
+        out.append(frame)
+    return out

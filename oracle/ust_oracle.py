@@ -30,7 +30,7 @@ __all__ = [
     "chunk_positions", "slot_of_frame", "window_frames", "window_slots",
     "KVCache", "kv_append", "window_attn", "lowrank_proj", "clip_schedule",
     "RAW_STEPS_4", "RAW_STEPS_2", "shifted_sigma", "dit_label", "flow_step",
-    "sample_chunk", "rne_bf16",
+    "sample_chunk", "rne_bf16", "conv3d_causal",
 ]
 
 
@@ -360,3 +360,38 @@ def rne_bf16(x: np.ndarray) -> np.ndarray:
     r = np.round(scaled)                # numpy rounds half to even
     out = np.ldexp(r, e - 8)
     return np.where(np.isfinite(x), out, x)
+
+
+# ------------------------------------------------------------------ decoder
+# UnStep, abstract: the runtime stack also speeds up VAE decoding, with an
+# optimised memory layout, precision and convolution kernels; Table 3: the
+# decoder turns the 1x21x16x60x104 latent into 81 frames of 832x480.  The
+# decoder's architecture is not on the pages.
+# READING: the decoder's convolutions are causal in time (a causal video
+# model decodes frames in order): output frame t sees input frames t-2, t-1,
+# t, with frames before the first taken as zero; 3x3 in space with zero
+# padding, so each frame keeps its size; stride 1.
+# Layout here: activations [T][H][W][C] (channels last), weights
+# [Cout][3][3][3][Cin] (time, row, column offsets), bias [Cout].
+
+def conv3d_causal(x: np.ndarray, w: np.ndarray,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t, y, x, o] = bias[o] + sum over dt, dy, dx, i of
+    w[o, dt, dy, dx, i] * x[t + dt - 2, y + dy - 1, x + dx - 1, i], with x
+    zero outside its frames, rows and columns.  fp64; one matrix product per
+    kernel tap over the zero-padded input."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T, H, W, Ci = x.shape
+    Co = w.shape[0]
+    assert w.shape == (Co, 3, 3, 3, Ci)
+    xp = np.zeros((T + 2, H + 2, W + 2, Ci))
+    xp[2:, 1:H + 1, 1:W + 1] = x
+    out = np.zeros((T, H, W, Co))
+    for dt in range(3):
+        for dy in range(3):
+            for dx in range(3):
+                out += xp[dt:dt + T, dy:dy + H, dx:dx + W] @ w[:, dt, dy, dx, :].T
+    if bias is not None:
+        out += np.asarray(bias, dtype=np.float64)
+    return out

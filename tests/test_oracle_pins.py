@@ -557,3 +557,70 @@ def test_sampler_matches_scalar_brute_force():
                                        [z.tolist() for z in noises], steps, s_star)
         assert np.max(np.abs(a - np.array(b))) < 1e-12
         assert np.allclose(la, lb, rtol=0, atol=1e-15) and np.allclose(ta, tb, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ decoder convolution
+
+def _conv_inputs(T, H, W, Ci, Co, seed):
+    rs = np.random.default_rng(seed)
+    return rs.standard_normal((T, H, W, Ci)), rs.standard_normal((Co, 3, 3, 3, Ci)), \
+        rs.standard_normal(Co)
+
+
+def test_conv3d_matches_scalar_brute_force():
+    """The causal 3-D convolution against scalar loops over the input
+    positions each output reads (Ci != Co, so transposed weights show)."""
+    x, w, b = _conv_inputs(4, 3, 5, 3, 2, 0)
+    got = O.conv3d_causal(x, w, b)
+    ref = np.array(brute.conv3d_causal(x.tolist(), w.tolist(), b.tolist()))
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_conv3d_delta_kernels_copy_and_shift():
+    """A kernel that is the identity at one tap copies the input shifted by
+    that tap: the current frame's centre copies it exactly; two frames back
+    delays it by two frames with zeros before (causal, no future frame
+    read); a corner tap shifts it in space with zeros at the border."""
+    T, H, W, C = 5, 4, 6, 3
+    x = np.random.default_rng(1).standard_normal((T, H, W, C))
+
+    def delta(dt, dy, dx):
+        w = np.zeros((C, 3, 3, 3, C))
+        w[:, dt, dy, dx, :] = np.eye(C)
+        return w
+    assert np.array_equal(O.conv3d_causal(x, delta(2, 1, 1)), x)
+    want = np.zeros_like(x)
+    want[2:] = x[:-2]
+    assert np.array_equal(O.conv3d_causal(x, delta(0, 1, 1)), want)
+    # tap (dt, dy, dx) = (2, 0, 2): out[t, y, x] = x[t, y - 1, x + 1]
+    want = np.zeros_like(x)
+    want[:, 1:, :-1] = x[:, :-1, 1:]
+    assert np.array_equal(O.conv3d_causal(x, delta(2, 0, 2)), want)
+    # bias only
+    b = np.arange(C, dtype=np.float64)
+    assert np.array_equal(O.conv3d_causal(x, np.zeros((C, 3, 3, 3, C)), b),
+                          np.broadcast_to(b, x.shape))
+
+
+def test_conv3d_is_causal_in_time():
+    """Changing frames t0 and later leaves every earlier output frame as it was."""
+    x, w, b = _conv_inputs(6, 3, 4, 4, 5, 2)
+    y1 = O.conv3d_causal(x, w, b)
+    x2 = x.copy()
+    x2[3:] = np.random.default_rng(3).standard_normal(x2[3:].shape)
+    y2 = O.conv3d_causal(x2, w, b)
+    assert np.array_equal(y1[:3], y2[:3])
+    assert not np.allclose(y1[3:], y2[3:])
+
+
+def test_conv3d_equals_torch_conv3d_on_padded_input():
+    """A library special case: torch's conv3d (fp64, CPU) over the input padded
+    with two zero frames in front and one zero row / column on each side."""
+    import torch
+    import torch.nn.functional as F
+    x, w, b = _conv_inputs(5, 6, 7, 8, 16, 4)
+    xt = torch.from_numpy(x).permute(3, 0, 1, 2)[None]           # [1][Ci][T][H][W]
+    xt = F.pad(xt, (1, 1, 1, 1, 2, 0))                            # W, H, then T (front only)
+    wt = torch.from_numpy(w).permute(0, 4, 1, 2, 3)               # [Co][Ci][3][3][3]
+    ref = F.conv3d(xt, wt, torch.from_numpy(b))[0].permute(1, 2, 3, 0).numpy()
+    assert np.max(np.abs(O.conv3d_causal(x, w, b) - ref)) < 1e-11
