@@ -23,7 +23,7 @@ OBJ = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["ust_host.cpp", "rope_table.hip", "kv_append.hip", "window_attn.hip", "sampler.hip",
-           "gemm.hip", "calib.hip"]
+           "gemm.hip", "calib.hip", "conv3d.hip"]
 # sources whose inline-asm global->LDS loads take a scalar base address
 DMA_SOURCES = ["window_attn.hip", "gemm.hip"]
 

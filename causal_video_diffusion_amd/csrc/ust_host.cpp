@@ -539,4 +539,28 @@ ust_status ust_calib_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out,
   }
 }
 
+ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, void* y,
+                             int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
+                             hipStream_t stream) {
+  try {
+    if (!x || !w || !y) return fail(UST_E_NULL, "x, w or y is NULL");
+    if (T <= 0 || H <= 0 || W <= 0 || Ci <= 0 || Co <= 0)
+      return fail(UST_E_SHAPE, "sizes must be positive (T=%d H=%d W=%d Ci=%d Co=%d)", T, H, W,
+                  Ci, Co);
+    if (int64_t(T) * H * W >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "T*H*W = %lld positions: at most 2^31 - 1",
+                  static_cast<long long>(int64_t(T) * H * W));
+    if (Ci != 16 && Ci != 32 && Ci != 64 && Ci != 128)
+      return fail(UST_E_UNSUPPORTED, "Ci %d: 16, 32, 64 or 128 supported", Ci);
+    if (Co % 128 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 128 supported", Co);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    ust::ConvArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
+                    static_cast<uint16_t*>(y), T, H, W, Ci, Co};
+    return hip_status(ust::launch_conv3d_causal(a, stream), "conv3d_causal launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
 }  // extern "C"

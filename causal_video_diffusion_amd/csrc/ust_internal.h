@@ -89,7 +89,18 @@ struct FlowStepArgs {
   float sigma, sigma_next, keep;
 };
 
+// Causal 3-D convolution (conv3d.hip); validated: Ci in {16, 32, 64, 128},
+// Co a multiple of 128, 16-byte aligned pointers, T*H*W < 2^31
+struct ConvArgs {
+  const uint16_t* x;         // [T][H][W][Ci] bf16
+  const uint16_t* w;         // [Co][3][3][3][Ci] bf16
+  const float* bias;         // [Co] or nullptr
+  uint16_t* y;               // [T][H][W][Co] bf16
+  int32_t T, H, W, Ci, Co;
+};
+
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);
+hipError_t launch_conv3d_causal(const ConvArgs& a, hipStream_t s);
 hipError_t launch_flow_step(const FlowStepArgs& a, hipStream_t s);
 // X [M][K] W [3HD][K]^T with the QKV epilogue; K % 64 == 0, D in {64, 128}
 hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_t s);

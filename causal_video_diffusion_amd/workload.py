@@ -237,3 +237,59 @@ def svd_factors_bf16(w: Workload, tag: int, rank: int, layer: int = 0):
     A, B = svd_factors_f64(w, tag, rank, layer)
     return (f32_to_bf16_bits(A.astype(np.float32)),
             f32_to_bf16_bits(B.astype(np.float32)))
+
+
+# ---------------------------------------------------------------- decoder convolution
+# The decoder runtime stack's convolution (UnStep, abstract; Table 3 fixes
+# the decoder's input, 21 latent frames of 16 x 60 x 104, and its output, 81
+# frames of 832 x 480).  Channel counts inside the decoder are not on the
+# pages: 128 is this workload's reading.
+
+TAG_CONV_X = 20
+TAG_CONV_W = 21
+TAG_CONV_B = 22
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    """One causal 3x3x3 convolution: input [T][H][W][ci] -> output [T][H][W][co]."""
+
+    wid: int
+    name: str
+    T: int
+    H: int
+    W: int
+    ci: int
+    co: int
+
+    @property
+    def positions(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.positions * self.co * 27 * self.ci
+
+
+CONV_TINY = ConvWorkload(wid=40, name="conv_tiny", T=3, H=5, W=7, ci=16, co=128)
+# a ragged last tile of positions, two blocks of output channels
+CONV_MID = ConvWorkload(wid=41, name="conv_mid", T=4, H=9, W=13, ci=64, co=256)
+# the decoder's first convolution: the 16-channel latent at 21 x 60 x 104
+VAE_CONV_IN = ConvWorkload(wid=42, name="vae_conv_in", T=21, H=60, W=104, ci=16, co=128)
+# a convolution inside the decoder at the latent resolution, 128 -> 128
+VAE_CONV = ConvWorkload(wid=43, name="vae_conv", T=21, H=60, W=104, ci=128, co=128)
+
+CONV_ALL = {c.name: c for c in (CONV_TINY, CONV_MID, VAE_CONV_IN, VAE_CONV)}
+
+
+def conv_tensors(c: ConvWorkload):
+    """Input x ~ N(0, 1) and weights w ~ N(0, 1/(27 ci)) as bf16 bits
+    ([T][H][W][ci], [co][3][3][3][ci]), bias ~ N(0, 0.01) fp32 [co]."""
+    gx = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0, c.wid, TAG_CONV_X])))
+    gw = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0, c.wid, TAG_CONV_W])))
+    gb = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0, c.wid, TAG_CONV_B])))
+    x = f32_to_bf16_bits(gx.standard_normal((c.T, c.H, c.W, c.ci), dtype=np.float32))
+    w = gw.standard_normal((c.co, 3, 3, 3, c.ci), dtype=np.float32)
+    w = f32_to_bf16_bits((w.astype(np.float64) / np.sqrt(27.0 * c.ci)).astype(np.float32))
+    b = (gb.standard_normal(c.co, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    return x, w, b

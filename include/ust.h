@@ -27,6 +27,8 @@
  *   ust_flow_step         one step of the chunk sampler: denoised estimate and
  *                         renoising (Table 4; abstract)
  *   ust_sigma_schedule    the sampler's noise levels (host only; Table 4)
+ *   ust_conv3d_causal     the decoder's causal 3-D convolution, channels last
+ *                         (abstract: VAE decoding runtime stack; Table 3)
  *
  * Conventions (all entry points):
  *  - Device pointers are caller-owned.  The library never allocates, frees
@@ -300,6 +302,28 @@ ust_status ust_lowrank_proj_static(const void* x, const void* a, const void* b,
 ust_status ust_flow_step(const float* x, const void* v, const float* noise, float sigma,
                          float sigma_next, float* x0_out, float* x_next, int64_t n,
                          hipStream_t stream);
+
+/* Causal 3-D convolution, the convolution kernel of the decoder runtime
+ * stack (abstract: VAE decoding with an optimised memory layout, precision
+ * and convolution kernels; Table 3: the decoder turns 21 latent frames of
+ * 16 x 60 x 104 into 81 frames of 832 x 480).  The decoder's architecture is
+ * not given; this is its 3x3x3 convolution, causal in time:
+ *   y[t][r][c][o] = bias[o] + sum over dt, dr, dc in {0,1,2} and i of
+ *                   w[o][dt][dr][dc][i] x[t+dt-2][r+dr-1][c+dc-1][i]
+ * with x zero outside its frames, rows and columns (output frame t reads
+ * input frames t-2 .. t; each frame keeps its size; stride 1).
+ *   x:    bf16 [T][H][W][Ci] (channels last), read.
+ *   w:    bf16 [Co][3][3][3][Ci], read.
+ *   bias: fp32 [Co] or NULL.
+ *   y:    bf16 [T][H][W][Co], written; must not overlap x.
+ * Arithmetic: bf16 MFMA with fp32 accumulation, the output rounded to bf16
+ * once (bias added in fp32).
+ * Errors: NULL x, w or y (UST_E_NULL); a non-positive size or T*H*W of 2^31
+ * or more (UST_E_SHAPE); Ci not 16, 32, 64 or 128, or Co not a multiple of
+ * 128 (UST_E_UNSUPPORTED); a pointer not 16-byte aligned (UST_E_ALIGN). */
+ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, void* y,
+                             int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
+                             hipStream_t stream);
 
 /* ---- host-only helpers (no GPU needed) ---- */
 

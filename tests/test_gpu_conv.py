@@ -1,0 +1,83 @@
+"""GPU parity of the decoder convolution (ust_conv3d_causal) against the
+fp64 oracle on the same bf16 inputs: max-abs 2e-2 and relative L2 1e-2, all
+outputs; bit-exact where the arithmetic is exact (a delta kernel copies or
+shifts the input: one product by 1.0 per output, then one rounding to bf16
+of a bf16 value)."""
+import numpy as np
+import pytest
+import torch
+
+from causal_video_diffusion_amd import _binding as B
+from causal_video_diffusion_amd import path as P
+from causal_video_diffusion_amd import workload as wl
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load()
+
+
+def _conv_gpu(c, x_bits, w_bits, bias):
+    x = P.to_device_bf16(x_bits)
+    w = P.to_device_bf16(w_bits)
+    b = torch.from_numpy(bias).cuda() if bias is not None else None
+    y = torch.full((c.T, c.H, c.W, c.co), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.ust_conv3d_causal(x, w, b, y, c.T, c.H, c.W, c.ci, c.co)
+    torch.cuda.synchronize()
+    return P.from_device_bf16(y)
+
+
+@pytest.mark.parametrize("name", ["conv_tiny", "conv_mid", "vae_conv_in", "vae_conv"])
+def test_conv3d_matches_oracle(name):
+    c = wl.CONV_ALL[name]
+    print(f"[conv3d {name}: {c.T}x{c.H}x{c.W}, {c.ci} -> {c.co}]", flush=True)
+    x, w, b = wl.conv_tensors(c)
+    got = wl.bf16_bits_to_f64(_conv_gpu(c, x, w, b))
+    ref = O.conv3d_causal(wl.bf16_bits_to_f64(x), wl.bf16_bits_to_f64(w), b.astype(np.float64))
+    assert np.isfinite(got).all()
+    d = got - ref
+    ma = float(np.abs(d).max())
+    rl = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    print(f"  {name}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert ma <= 2e-2 and rl <= 1e-2
+    # the first frames see no earlier frames: frame 0 must equal the
+    # convolution of frame 0 alone
+    ref0 = O.conv3d_causal(wl.bf16_bits_to_f64(x)[:1], wl.bf16_bits_to_f64(w), b.astype(np.float64))
+    assert np.max(np.abs(got[:1] - ref0)) <= 2e-2
+
+
+@pytest.mark.parametrize("tap", [(2, 1, 1), (0, 1, 1), (1, 0, 2)])
+def test_conv3d_delta_kernel_is_exact(tap):
+    """Identity weights at one tap: the output is the input shifted by the
+    tap, bit for bit, zero where the shift leaves the input."""
+    c = wl.ConvWorkload(wid=44, name="conv_delta", T=5, H=9, W=13, ci=128, co=128)
+    x, _, _ = wl.conv_tensors(c)
+    w = np.zeros((c.co, 3, 3, 3, c.ci), np.uint16)
+    dt, dy, dx = tap
+    w[np.arange(c.co), dt, dy, dx, np.arange(c.ci)] = 0x3F80          # 1.0
+    got = _conv_gpu(c, x, w, None)
+    want = np.zeros_like(x)
+    st, sy, sx = dt - 2, dy - 1, dx - 1                               # input offset of the tap
+    T, H, W = c.T, c.H, c.W
+    want[max(0, -st):T - max(0, st), max(0, -sy):H - max(0, sy), max(0, -sx):W - max(0, sx)] = \
+        x[max(0, st):T + min(0, st), max(0, sy):H + min(0, sy), max(0, sx):W + min(0, sx)]
+    assert np.array_equal(got, want)
+
+
+def test_conv3d_deterministic_and_causal():
+    """Two runs agree bit for bit; changing frames 2 and later leaves output
+    frames 0 and 1 bit-identical."""
+    c = wl.CONV_MID
+    x, w, b = wl.conv_tensors(c)
+    y1 = _conv_gpu(c, x, w, b)
+    y2 = _conv_gpu(c, x, w, b)
+    assert np.array_equal(y1, y2)
+    x2 = x.copy()
+    x2[2:] = wl.f32_to_bf16_bits(np.random.default_rng(5).standard_normal(x2[2:].shape).astype(np.float32))
+    y3 = _conv_gpu(c, x2, w, b)
+    assert np.array_equal(y1[:2], y3[:2])
+    assert not np.array_equal(y1[2:], y3[2:])

@@ -40,7 +40,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 16
+    assert len(syms) == 17
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -180,6 +180,19 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     st, msg = _raw(lib, "ust_lowrank_proj_static", fake, fake, fake, None, fake, big_m, 64, 64,
                    64, None)
     assert st == "UST_E_RANGE" and "static scratch" in msg
+    # the decoder convolution
+    assert _raw(lib, "ust_conv3d_causal", None, fake, None, fake, 2, 3, 4, 16, 128,
+                None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 0, 3, 4, 16, 128,
+                None)[0] == "UST_E_SHAPE"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 48, 128,
+                None)[0] == "UST_E_UNSUPPORTED"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 16, 96,
+                None)[0] == "UST_E_UNSUPPORTED"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake + 8, None, fake, 2, 3, 4, 16, 128,
+                None)[0] == "UST_E_ALIGN"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2048, 1024, 1024, 16, 128,
+                None)[0] == "UST_E_SHAPE"
     # frames outside the table
     assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 21, 19, None)[0] == "UST_E_RANGE"
     assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake, None,
