@@ -25,7 +25,7 @@ ARCH = "gfx950"
 SOURCES = ["ust_host.cpp", "rope_table.hip", "kv_append.hip", "window_attn.hip", "sampler.hip",
            "gemm.hip", "calib.hip", "conv3d.hip"]
 # sources whose inline-asm global->LDS loads take a scalar base address
-DMA_SOURCES = ["window_attn.hip", "gemm.hip"]
+DMA_SOURCES = ["window_attn.hip", "gemm.hip", "conv3d.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]

@@ -6,23 +6,28 @@
 //
 // Layout and precision: activations channels last [T][H][W][C] bf16, weights
 // [Cout][3][3][3][Cin] bf16, bias fp32, fp32 accumulation, bf16 out.  With
-// the channels innermost, 8 consecutive input channels of one position are
-// one 16-byte load, which is exactly a lane's share of an MFMA operand.
+// the channels innermost, the input rows a tap needs are one contiguous
+// block of memory for a run of consecutive positions.
 //
 // Implicit GEMM on bf16 MFMA 32x32x16: out^T[co][p] = sum over taps and
-// 16-channel steps of W[co][tap][ci] x[p shifted by the tap][ci].
-//  * A operand, the weights: one tap's [128 co][Cin] block per step, staged
-//    global -> registers -> LDS (two buffers, 16-byte chunks XOR-swizzled by
-//    row so each MFMA operand read hits distinct banks) and shared by the
-//    workgroup's 8 waves.
-//  * B operand, the input: each lane loads its own position's 8 channels at
-//    the tap's offset straight into registers (zero outside the input),
-//    four k-steps ahead of the MFMA that uses them.
-//  * A workgroup owns 256 consecutive positions of the flattened (t, y, x)
-//    grid (32 per wave) and 128 output channels; workgroups are ordered so
-//    that each XCD takes a contiguous run of positions.
+// channels of W[co][tap][ci] x[p shifted by the tap][ci].
+//  * A workgroup owns 512 consecutive positions of the flattened (t, y, x)
+//    grid (64 per wave, two 32-position blocks) and 128 output channels
+//    (four 32-channel blocks): 8 MFMAs per 16 channels, each input fragment
+//    used 4 times and each weight fragment twice.
+//  * Work runs in stages of one (frame offset dt, row offset dy) and CQ
+//    input channels: the 514 input positions the three column offsets dx
+//    need (one contiguous block, clamped to the tensor) and the three taps'
+//    weights go global -> LDS (global_load_lds, coalesced 64-byte rows,
+//    16-byte chunks XOR-swizzled so operand reads hit distinct banks),
+//    double-buffered: stage s+1 loads while stage s computes.
+//  * Taps that leave the input (frames before the first, rows off the
+//    frame, columns that would wrap into the next row) are zeroed per
+//    position after the fragment read.
 //  * Each lane ends with 4 consecutive output channels of one position per
 //    register group: 8-byte stores.
+
+#include <type_traits>
 
 #include "ust_device.h"
 #include "ust_internal.h"
@@ -31,8 +36,9 @@ namespace ust {
 namespace {
 
 constexpr int kConvWaves = 8;
-constexpr int kConvCo = 128;   // output channels per workgroup
-constexpr int kConvPf = 4;     // input fragments in flight per wave
+constexpr int kConvCo = 128;               // output channels per workgroup
+constexpr int kConvPos = 64 * kConvWaves;  // positions per workgroup
+constexpr int kConvRows = kConvPos + 32;   // staged input rows (514 used; whole 1 KB loads)
 
 __device__ __forceinline__ int conv_xcd_remap(int b, int nb) {
   const int q = nb / 8, rem = nb % 8;
@@ -40,126 +46,171 @@ __device__ __forceinline__ int conv_xcd_remap(int b, int nb) {
   return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + k;
 }
 
-// XOR key of weight row `row` for rows of nch 16-byte chunks (a power of
-// two): the 16 rows one 16-lane group reads land on 16 distinct bank groups
-__device__ __forceinline__ int conv_key(int row, int nch) {
-  return nch >= 16 ? (row & 15) : ((row / (16 / nch)) & (nch - 1));
+__device__ __forceinline__ uint32_t conv_lds_addr(const uint16_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
+}
+// 16 bytes per lane, global -> LDS at m0 + 16 * lane.  The base is made
+// wave-uniform through readfirstlane; the asm starts with s_nop 4 because a
+// vector instruction's write of a scalar register is not interlocked with a
+// vector memory read of it (5 wait states) and the compiler adds none
+// before inline asm.
+__device__ __forceinline__ void conv_load_lds16(const uint16_t* sbase, uint32_t voff_bytes, uint32_t m0) {
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t su = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(p >> 32)))) << 32) |
+                      uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(p))));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes),
+               "s"(reinterpret_cast<const uint16_t*>(su)), "{m0}"(m0));
+}
+__device__ __forceinline__ void conv_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (0 << 14));   // vmcnt(0) lgkmcnt(0)
+}
+__device__ __forceinline__ void conv_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// XOR key of a staged row of NCH 16-byte chunks (2 or 4): the 16
+// consecutive rows one 16-lane group reads land on 16 distinct bank groups
+template <int NCH>
+__device__ __forceinline__ int conv_key(int row) {
+  if constexpr (NCH == 4) return (row >> 2) & 3;
+  else return (row >> 3) & 1;
 }
 
 template <int Ci>
 __global__ void __launch_bounds__(64 * kConvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 conv3d_causal_kernel(ConvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wl[2 * kConvCo * Ci];   // two taps' weights
+  constexpr int CQ = Ci < 32 ? Ci : 32;       // input channels per stage
+  constexpr int NCH = CQ / 8;                 // 16-byte chunks per staged row
+  constexpr int NQ = Ci / CQ;                 // channel groups
+  constexpr int NSTAGE = 9 * NQ;              // (dt, dy, channel group)
+  constexpr int KS = CQ / 16;                 // k-steps per tap per stage
+  constexpr int IN_EL = kConvRows * CQ;       // input block elements
+  constexpr int W_EL = 3 * kConvCo * CQ;      // three taps' weights
+  constexpr int BUF = IN_EL + W_EL;
+  constexpr int IN_LOADS = IN_EL * 2 / 1024;  // 1 KB loads per stage
+  constexpr int W_LOADS = W_EL * 2 / 1024;
+  constexpr int NLOADS = IN_LOADS + W_LOADS;
+  constexpr int LPW = (NLOADS + kConvWaves - 1) / kConvWaves;
+  static_assert(IN_EL * 2 % 1024 == 0 && W_EL * 2 % 1024 == 0, "whole 1 KB loads");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * BUF];
+
   const int Co = a.Co;
-  constexpr int nch = Ci / 8;             // 16-byte chunks per weight row
-  constexpr int nks = Ci / 16;            // k-steps per tap
-  constexpr int total = 27 * nks;         // k-steps in all
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int HW = a.H * a.W;
-  const int64_t P = int64_t(a.T) * HW;
-  const int ntile = int((P + 255) / 256);
+  const int P = a.T * HW;
+  const int ntile = (P + kConvPos - 1) / kConvPos;
   const int tile = conv_xcd_remap(blockIdx.x, ntile);
   const int co0 = blockIdx.y * kConvCo;
+  const int p0 = tile * kConvPos;
 
-  // this lane's position and the taps that stay inside the input
-  const int64_t p = int64_t(tile) * 256 + wave * 32 + l32;
-  const bool pvalid = p < P;
-  const int pp = pvalid ? int(p) : 0;
-  const int pt = pp / HW, pr = pp - pt * HW, py = pr / a.W, px = pr - py * a.W;
-  uint32_t tapmask = 0;
+  // the taps each of this lane's two positions may read
+  uint32_t tapmask[2];
 #pragma unroll
-  for (int tap = 0; tap < 27; ++tap) {
-    const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
-    const int t2 = pt + dt - 2, y2 = py + dy - 1, x2 = px + dx - 1;
-    if (pvalid && t2 >= 0 && y2 >= 0 && y2 < a.H && x2 >= 0 && x2 < a.W) tapmask |= 1u << tap;
-  }
-  const uint16_t* xbase = a.x + int64_t(pp) * Ci + 8 * half;
-
-  // input fragment of flattened k-step s (tap s / nks, channels 16 (s % nks) ..)
-  auto load_in = [&](int s) __attribute__((always_inline)) -> uint4 {
-    const int tap = s / nks, c = s - tap * nks;
-    const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
-    const int64_t delta = (int64_t(dt - 2) * HW + (dy - 1) * a.W + (dx - 1)) * Ci + 16 * c;
-    const bool ok = (tapmask >> tap) & 1u;
-    const uint4 v = *reinterpret_cast<const uint4*>(xbase + (ok ? delta : int64_t(16 * c)));
-    return ok ? v : make_uint4(0, 0, 0, 0);
-  };
-
-  // weights of one tap: chunk q of the [128][Ci] block
-  constexpr int wchunks = kConvCo * nch;
-  constexpr int wper = (wchunks + 64 * kConvWaves - 1) / (64 * kConvWaves);
-  uint4 wreg[wper];
-  auto load_w = [&](int tap) __attribute__((always_inline)) {
+  for (int pb = 0; pb < 2; ++pb) {
+    const int p = p0 + wave * 64 + pb * 32 + l32;
+    uint32_t m = 0;
+    if (p < P) {
+      const int pt = p / HW, pr = p - pt * HW, py = pr / a.W, px = pr - py * a.W;
 #pragma unroll
-    for (int i = 0; i < wper; ++i) {
-      const int q = tid + i * 64 * kConvWaves;
-      if (q < wchunks) {
-        const int row = q / nch, c = q - row * nch;
-        wreg[i] = *reinterpret_cast<const uint4*>(a.w + (int64_t(co0 + row) * 27 + tap) * Ci + c * 8);
+      for (int tap = 0; tap < 27; ++tap) {
+        const int t2 = pt + tap / 9 - 2, y2 = py + (tap / 3) % 3 - 1, x2 = px + tap % 3 - 1;
+        if (t2 >= 0 && y2 >= 0 && y2 < a.H && x2 >= 0 && x2 < a.W) m |= 1u << tap;
       }
     }
-  };
-  auto store_w = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* dst = wl + buf * kConvCo * Ci;
-#pragma unroll
-    for (int i = 0; i < wper; ++i) {
-      const int q = tid + i * 64 * kConvWaves;
-      if (q < wchunks) {
-        const int row = q / nch, c = q - row * nch;
-        *reinterpret_cast<uint4*>(dst + row * Ci + ((c ^ conv_key(row, nch)) * 8)) = wreg[i];
-      }
-    }
-  };
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-
-  uint4 inq[kConvPf];
-#pragma unroll
-  for (int i = 0; i < kConvPf; ++i) inq[i] = i < total ? load_in(i) : make_uint4(0, 0, 0, 0);
-  load_w(0);
-  store_w(0);
-  __syncthreads();
-
-  int s = 0;
-  for (int tap = 0; tap < 27; ++tap) {
-    const int buf = tap & 1;
-    if (tap + 1 < 27) load_w(tap + 1);   // lands in registers while this tap computes
-    const uint16_t* W = wl + buf * kConvCo * Ci;
-#pragma unroll
-    for (int c = 0; c < nks; ++c, ++s) {
-      const bf16x8 bf = as_bf16x8(inq[0]);
-#pragma unroll
-      for (int i = 0; i + 1 < kConvPf; ++i) inq[i] = inq[i + 1];
-      inq[kConvPf - 1] = s + kConvPf < total ? load_in(s + kConvPf) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int row = 32 * b + l32;
-        const bf16x8 af = as_bf16x8(
-            *reinterpret_cast<const uint4*>(W + row * Ci + (((2 * c + half) ^ conv_key(row, nch)) * 8)));
-        acc[b] = mfma32(af, bf, acc[b]);
-      }
-    }
-    if (tap + 1 < 27) store_w(buf ^ 1);   // the other buffer was last read a tap ago
-    __syncthreads();
+    tapmask[pb] = m;
   }
 
-  // lane: position p, output channels co0 + 32 b + 8 (r / 4) + 4 half + r % 4
-  if (pvalid) {
-    uint16_t* yp = a.y + p * Co + co0;
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(conv_lds_addr(lds));
+  // stage s: (dt, dy) = (s / NQ) / 3, % 3; channels CQ * (s % NQ) ..
+  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+    const int dtdy = s / NQ, q = s - dtdy * NQ;
+    const int dt = dtdy / 3, dy = dtdy - 3 * dt;
+    const int shift = (dt - 2) * HW + (dy - 1) * a.W - 1;   // input position of local row 0
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int li = wave * LPW + i;                        // 1 KB load index
+      if (li < NLOADS) {
+        const int e = li * 512 + lane * 8;                  // element of this lane's chunk
+        const uint32_t dst = lds_base + uint32_t(buf * BUF + li * 512) * 2u;
+        if (li < IN_LOADS) {
+          const int row = e / CQ, cp = (e % CQ) / 8;
+          const int c = cp ^ conv_key<NCH>(row);
+          int pos = p0 + shift + row;
+          pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);      // clamped; such taps are masked
+          conv_load_lds16(a.x, uint32_t((pos * Ci + q * CQ + c * 8) * 2), dst);
+        } else {
+          const int ew = e - IN_EL;
+          const int row = ew / CQ, cp = (ew % CQ) / 8;       // row = dx * 128 + co
+          const int c = cp ^ conv_key<NCH>(row);
+          const int dx = row / kConvCo, co = row - dx * kConvCo;
+          const int tap = dt * 9 + dy * 3 + dx;
+          conv_load_lds16(a.w, uint32_t((((co0 + co) * 27 + tap) * Ci + q * CQ + c * 8) * 2), dst);
+        }
+      }
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[pb][b][r] = 0.f;
+
+  auto compute = [&](int s, int buf) __attribute__((always_inline)) {
+    const int dtdy = s / NQ;
+    const uint16_t* X = lds + buf * BUF;
+    const uint16_t* Wt = X + IN_EL;
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx) {
+      const int tap = dtdy * 3 + dx;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        bf16x8 bfr[2], afr[4];
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+          const int row = wave * 64 + pb * 32 + l32 + dx;
+          uint4 v = *reinterpret_cast<const uint4*>(X + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8));
+          if (!((tapmask[pb] >> tap) & 1u)) v = make_uint4(0, 0, 0, 0);
+          bfr[pb] = as_bf16x8(v);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int row = dx * kConvCo + 32 * b + l32;
+          afr[b] = as_bf16x8(*reinterpret_cast<const uint4*>(Wt + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8)));
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int pb = 0; pb < 2; ++pb) acc[pb][b] = mfma32(afr[b], bfr[pb], acc[pb][b]);
+      }
+    }
+  };
+
+  issue(0, 0);
+  for (int s = 0; s < NSTAGE; ++s) {
+    conv_wait_all();     // this wave's loads of stage s have landed
+    conv_barrier();      // everyone's have, and stage s-1's buffer is free
+    if (s + 1 < NSTAGE) issue(s + 1, (s + 1) & 1);
+    compute(s, s & 1);
+  }
+
+  // lane: positions p0 + wave*64 + pb*32 + l32, output channels
+  // co0 + 32 b + 8 (r / 4) + 4 half + r % 4
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb) {
+    const int p = p0 + wave * 64 + pb * 32 + l32;
+    if (p >= P) continue;
+    uint16_t* yp = a.y + int64_t(p) * Co + co0;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int co = 32 * b + 8 * g + 4 * half;
-        float v[4] = {acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
+        float v[4] = {acc[pb][b][4 * g], acc[pb][b][4 * g + 1], acc[pb][b][4 * g + 2], acc[pb][b][4 * g + 3]};
         if (a.bias) {
           const float4 bb = *reinterpret_cast<const float4*>(a.bias + co0 + co);
           v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
@@ -173,7 +224,7 @@ conv3d_causal_kernel(ConvArgs a) {
 
 hipError_t launch_conv3d_causal(const ConvArgs& a, hipStream_t s) {
   const int64_t P = int64_t(a.T) * a.H * a.W;
-  const dim3 grid(unsigned((P + 255) / 256), unsigned(a.Co / kConvCo));
+  const dim3 grid(unsigned((P + kConvPos - 1) / kConvPos), unsigned(a.Co / kConvCo));
   const dim3 block(64 * kConvWaves);
   switch (a.Ci) {
     case 16: hipLaunchKernelGGL(conv3d_causal_kernel<16>, grid, block, 0, s, a); break;

@@ -553,6 +553,9 @@ ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, vo
     if (Ci != 16 && Ci != 32 && Ci != 64 && Ci != 128)
       return fail(UST_E_UNSUPPORTED, "Ci %d: 16, 32, 64 or 128 supported", Ci);
     if (Co % 128 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 128 supported", Co);
+    if (int64_t(T) * H * W * std::max(Ci, Co) >= (int64_t(1) << 30) ||
+        int64_t(Co) * 27 * Ci >= (int64_t(1) << 30))
+      return fail(UST_E_SHAPE, "tensors too large for 32-bit byte offsets");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
       return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
     ust::ConvArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
