@@ -59,7 +59,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=("wan_window", "wan_720p", "wan_clip", "wan_fused",
-                                            "wan_sampler"),
+                                            "wan_sampler", "vae_conv", "vae_conv_in"),
                     default="wan_window",
                     help="the windowed Wan2.1-1.3B layer-chunk (default); the same layer "
                          "at 720p (45x80 tokens/frame, rank 256); the whole 81-frame "
@@ -176,6 +176,8 @@ def main():
         return main_fused(args)
     if args.workload == "wan_sampler":
         return main_sampler(args)
+    if args.workload in ("vae_conv", "vae_conv_in"):
+        return main_conv(args)
     w = wl.ALL[args.workload]
     C = 5                                   # last chunk prepared
     # Steady-state chunks timed in turn.  The windowed layer's 21-slot ring
@@ -672,6 +674,108 @@ def main_sampler(args):
             "kind": "oracle", "ms_per_step": round(cpu_s * 1e3, 1),
             "sample": f"the whole clip's 23 flow steps in fp64 NumPy, {reps} times; value = the "
                       "same algorithmic bytes / wall time (elementwise NumPy is single-threaded)",
+        }
+    print(json.dumps(result), flush=True)
+
+
+def main_conv(args):
+    """One causal 3x3x3 convolution of the decoder runtime stack (UnStep,
+    abstract: VAE decoding with an optimised memory layout, precision and
+    convolution kernels; Table 3: the decoder's input is 21 latent frames of
+    16 x 60 x 104): channels last, bf16 with fp32 accumulation, at the latent
+    resolution; vae_conv is 128 -> 128 channels, vae_conv_in the decoder's
+    first convolution, 16 -> 128 (channel counts are a reading).  A step is
+    one convolution."""
+    import numpy as np
+    import torch
+
+    from causal_video_diffusion_amd import _binding as B
+    from causal_video_diffusion_amd import path as P
+    from causal_video_diffusion_amd import workload as wl
+
+    c = wl.CONV_ALL[args.workload]
+    stream = torch.cuda.current_stream()
+    x, w, b = wl.conv_tensors(c)
+    xd, wd, bd = P.to_device_bf16(x), P.to_device_bf16(w), torch.from_numpy(b).cuda()
+    y = torch.empty((c.T, c.H, c.W, c.co), dtype=torch.bfloat16, device="cuda")
+    calib = None if args.no_calib else calibrate(stream)
+
+    def step():
+        B.ust_conv3d_causal(xd, wd, bd, y, c.T, c.H, c.W, c.ci, c.co)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    each = [1000.0 * e[0].elapsed_time(e[1]) for e in evs]
+    kern_us = float(np.mean(each))
+    tflops = c.flops / (kern_us * 1e-6) / 1e12
+    nbytes = 2 * c.positions * (c.ci + c.co) + 2 * c.co * 27 * c.ci + 4 * c.co
+    result = {
+        "metric": f"decoder causal conv3d TFLOP/s ({c.name}), % MFMA peak",
+        "value": round(c.flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.name}: causal 3x3x3 convolution, {c.T} frames x {c.H} x {c.W} "
+                        f"(the decoder's latent resolution, Table 3), {c.ci} -> {c.co} channels, "
+                        f"channels last, bf16 in and out, fp32 accumulation, bias; a step is "
+                        f"one convolution",
+            "gflop": round(c.flops / 1e9, 2), "algorithmic_MB": round(nbytes / 1e6, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": f"conv3d_causal_kernel<{c.ci}>",
+            "kernel_us": round(kern_us, 2),
+            "kernel_us_spread": pct(each),
+        },
+    }
+    if calib is not None:
+        result["calibration"] = calib
+        result["roofline"]["measured_peak"] = calib["mfma_bf16_TFLOPs"]
+        result["roofline"]["frac_of_measured_peak"] = round(tflops / calib["mfma_bf16_TFLOPs"], 4)
+    if not args.no_cpu_baseline:
+        import oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = 1
+        xf, wf = wl.bf16_bits_to_f64(x), wl.bf16_bits_to_f64(w)
+        bf = b.astype(np.float64)
+        reps = 2
+        tc = time.perf_counter()
+        for _ in range(reps):
+            O.conv3d_causal(xf, wf, bf)
+        cpu_s = (time.perf_counter() - tc) / reps
+        result["cpu_baseline"] = {
+            "value": round(c.flops / cpu_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "ms_per_step": round(cpu_s * 1e3, 1),
+            "sample": f"the whole convolution in fp64 NumPy (27 matrix products over the "
+                      f"zero-padded input), {reps} times; cores = BLAS threads",
         }
     print(json.dumps(result), flush=True)
 
