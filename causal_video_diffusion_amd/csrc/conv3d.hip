@@ -61,6 +61,14 @@ __device__ __forceinline__ void conv_load_lds16(const uint16_t* sbase, uint32_t 
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes),
                "s"(reinterpret_cast<const uint16_t*>(su)), "{m0}"(m0));
 }
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ void conv_wait_all() {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (0 << 8) | (0 << 14));   // vmcnt(0) lgkmcnt(0)
 }
@@ -124,12 +132,14 @@ conv3d_causal_kernel(ConvArgs a) {
 
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(conv_lds_addr(lds));
   // stage s: (dt, dy) = (s / NQ) / 3, % 3; channels CQ * (s % NQ) ..
-  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+  // loads I0 .. I1-1 (of LPW) of this wave's share of stage s into buffer buf
+  auto issue = [&](int s, int buf, auto i0c, auto i1c) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
     const int dtdy = s / NQ, q = s - dtdy * NQ;
     const int dt = dtdy / 3, dy = dtdy - 3 * dt;
     const int shift = (dt - 2) * HW + (dy - 1) * a.W - 1;   // input position of local row 0
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
+    for (int i = I0; i < I1; ++i) {
       const int li = wave * LPW + i;                        // 1 KB load index
       if (li < NLOADS) {
         const int e = li * 512 + lane * 8;                  // element of this lane's chunk
@@ -160,15 +170,22 @@ conv3d_causal_kernel(ConvArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[pb][b][r] = 0.f;
 
-  auto compute = [&](int s, int buf) __attribute__((always_inline)) {
+  // stage s from buffer buf; between its 3 KS steps of 8 MFMAs, this
+  // wave's loads of stage s + 1 (if any) go out a share at a time, so the
+  // waves of a SIMD do not all stall on load issue at once
+  constexpr int NSTEP = 3 * KS;
+  auto compute = [&](int s, int buf, bool next) __attribute__((always_inline)) {
     const int dtdy = s / NQ;
     const uint16_t* X = lds + buf * BUF;
     const uint16_t* Wt = X + IN_EL;
-#pragma unroll
-    for (int dx = 0; dx < 3; ++dx) {
+    static_for<0, NSTEP>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int dx = j / KS, k = j % KS;
       const int tap = dtdy * 3 + dx;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
+      if (next)
+        issue(s + 1, buf ^ 1, std::integral_constant<int, j * LPW / NSTEP>{},
+              std::integral_constant<int, (j + 1) * LPW / NSTEP>{});
+      {
         bf16x8 bfr[2], afr[4];
 #pragma unroll
         for (int pb = 0; pb < 2; ++pb) {
@@ -187,15 +204,14 @@ conv3d_causal_kernel(ConvArgs a) {
 #pragma unroll
           for (int pb = 0; pb < 2; ++pb) acc[pb][b] = mfma32(afr[b], bfr[pb], acc[pb][b]);
       }
-    }
+    });
   };
 
-  issue(0, 0);
+  issue(0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, LPW>{});
   for (int s = 0; s < NSTAGE; ++s) {
     conv_wait_all();     // this wave's loads of stage s have landed
     conv_barrier();      // everyone's have, and stage s-1's buffer is free
-    if (s + 1 < NSTAGE) issue(s + 1, (s + 1) & 1);
-    compute(s, s & 1);
+    compute(s, s & 1, s + 1 < NSTAGE);
   }
 
   // lane: positions p0 + wave*64 + pb*32 + l32, output channels
