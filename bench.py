@@ -113,9 +113,11 @@ def pct(xs):
 
 def calibrate(stream):
     """Rates this GPU sustains, measured in this process before the timed
-    region: the bf16 MFMA rate of a kernel that only issues MFMAs (one
-    workgroup of 8 waves per compute unit, ~10 ms), and a plain 1 GiB device
-    copy (bytes read + written per second)."""
+    region: the bf16 MFMA rate of a kernel that only issues MFMAs on
+    pseudo-random operands (one workgroup of 8 waves per compute unit,
+    ~10 ms; the power-limited clock makes the rate depend on the operands'
+    bits, and random ones are what real data looks like), and a plain 1 GiB
+    device copy (bytes read + written per second)."""
     import torch
     from causal_video_diffusion_amd import _binding as B
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -147,7 +149,8 @@ def calibrate(stream):
     del src, dst
     return {"mfma_bf16_TFLOPs": round(mfma_tflops, 1), "copy_GBs": round(copy_gbs, 1),
             "note": f"MFMA-only kernel (ust_calib_mfma_bf16: {cus} workgroups x 8 waves, 4 "
-                    f"independent 32x32x16 bf16 chains per wave, {reps} launches) and a 1 GiB "
+                    f"independent 32x32x16 bf16 chains per wave on pseudo-random operands, {reps} "
+                    f"launches) and a 1 GiB "
                     f"device copy (read + written bytes), both timed with HIP events in this "
                     f"process before the timed region"}
 

@@ -3,8 +3,10 @@
  *
  * Not steps of the attention path: a kernel that only issues bf16 MFMAs, so
  * that a benchmark can report the matrix rate the part sustains under load
- * (its shader clock then sits below the nominal one) beside the published
- * peak, and compare each kernel with both.  Same conventions as ust.h:
+ * beside the published peak, and compare each kernel with both.  The shader
+ * clock under a matrix load is power-limited and the power depends on the
+ * operands' bits, so the kernel feeds pseudo-random operands (random signs
+ * and mantissas, magnitude 0.5 .. 2), as a kernel on real data would see.  Same conventions as ust.h:
  * caller-owned device memory, asynchronous on `stream`, validation before
  * launch, status codes and ust_last_error().
  */
@@ -18,8 +20,9 @@ extern "C" {
 #endif
 
 /* Launch n_workgroups workgroups of 8 waves; every wave issues
- * iters x 4 independent v_mfma_f32_32x32x16_bf16 back to back and writes one
- * fp32 sum to out[workgroup * 8 + wave].
+ * iters x 4 independent v_mfma_f32_32x32x16_bf16 back to back, on four
+ * pseudo-random operand pairs in turn, and writes one fp32 sum to
+ * out[workgroup * 8 + wave].
  *   out: fp32 [n_workgroups * 8], written (the values carry no meaning).
  *   flops_out: host pointer or NULL; receives the launch's flop count,
  *              n_workgroups * 8 * iters * 4 * 32768.
