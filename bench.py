@@ -49,6 +49,11 @@ ATTN_TRAFFIC = {
     ("wan_window", "whole"): {"src_sha16": "5c8fcf3a7ae9e2c9",
                               "bytes": (2 * 108170 + 17700) * 1024},
 }
+# the decoder convolution, per workload, same scaling and keying
+CONV_SOURCES = ("conv3d.hip", "ust_device.h")
+CONV_TRAFFIC = {
+    "vae_conv": {"src_sha16": "48a41c536a7d7f76", "bytes": (2 * 61909 + 32760) * 1024},
+}
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
 # clean-cache ones do not: 892 KiB; every one writes 1170 KiB), same scaling
@@ -87,20 +92,43 @@ def attn_flops(n_q, n_k, d, h):
     return 4.0 * n_q * n_k * d * h      # QK^T and PV, 2 flop per multiply-add
 
 
-def attn_source_sha16():
-    """sha256 (first 16 hex digits) of the attention kernel's sources."""
+def source_sha16(names):
+    """sha256 (first 16 hex digits) of a kernel's sources under csrc/."""
     import hashlib
     hs = hashlib.sha256()
-    for name in ATTN_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "causal_video_diffusion_amd", "csrc", name), "rb") as f:
             hs.update(f.read())
     return hs.hexdigest()[:16]
+
+
+def attn_source_sha16():
+    """sha256 (first 16 hex digits) of the attention kernel's sources."""
+    return source_sha16(ATTN_SOURCES)
 
 
 def attn_traffic(workload, schedule):
     """Counter-measured bytes of the attention, if taken on these sources."""
     t = ATTN_TRAFFIC.get((workload, schedule))
     return t["bytes"] if t and t["src_sha16"] == attn_source_sha16() else None
+
+
+def conv_traffic(workload):
+    """Counter-measured bytes of the decoder convolution, if taken on these sources."""
+    t = CONV_TRAFFIC.get(workload)
+    return t["bytes"] if t and t["src_sha16"] == source_sha16(CONV_SOURCES) else None
+
+
+def reference_copy(mb):
+    """One plain device copy of `mb` MiB: the known-size reference the HBM
+    traffic counters are scaled by (its FETCH_SIZE and WRITE_SIZE)."""
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def pct(xs):
@@ -251,12 +279,7 @@ def main():
             ev[4].record(stream)
 
     if args.calib_copy_mb:
-        n = args.calib_copy_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        reference_copy(args.calib_copy_mb)
 
     calib = None if args.no_calib else calibrate(stream)
 
@@ -701,6 +724,8 @@ def main_conv(args):
     x, w, b = wl.conv_tensors(c)
     xd, wd, bd = P.to_device_bf16(x), P.to_device_bf16(w), torch.from_numpy(b).cuda()
     y = torch.empty((c.T, c.H, c.W, c.co), dtype=torch.bfloat16, device="cuda")
+    if args.calib_copy_mb:
+        reference_copy(args.calib_copy_mb)
     calib = None if args.no_calib else calibrate(stream)
 
     def step():
@@ -709,18 +734,19 @@ def main_conv(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for e in evs:
-        e[0].record(stream)
-        step()
-        e[1].record(stream)
-    t1.record(stream)
+    # events only between groups of G back-to-back launches: an event pair
+    # around every launch would add its own gap to a ~100 us kernel
+    G = 5
+    groups = max(1, args.steps // G)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    evs[0].record(stream)
+    for gi in range(groups):
+        for _ in range(G):
+            step()
+        evs[gi + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    each = [1000.0 * e[0].elapsed_time(e[1]) for e in evs]
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / (groups * G)
+    each = [1000.0 * evs[i].elapsed_time(evs[i + 1]) / G for i in range(groups)]
     kern_us = float(np.mean(each))
     tflops = c.flops / (kern_us * 1e-6) / 1e12
     nbytes = 2 * c.positions * (c.ci + c.co) + 2 * c.co * 27 * c.ci + 4 * c.co
@@ -729,7 +755,7 @@ def main_conv(args):
         "value": round(c.flops / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": groups * G,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
@@ -750,10 +776,12 @@ def main_conv(args):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": conv_traffic(args.workload),
             "kernel": f"conv3d_causal_kernel<{c.ci}>",
             "kernel_us": round(kern_us, 2),
             "kernel_us_spread": pct(each),
+            "timing": f"HIP events on the launch stream around groups of {G} back-to-back "
+                      f"launches; kernel_us = group time / {G} (includes the launch gaps)",
         },
     }
     if calib is not None:

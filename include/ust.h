@@ -344,11 +344,23 @@ ust_status ust_sigma_schedule(const int32_t* raw_steps, int32_t n, double shift,
                               int32_t n_train, double* sigma_out, double* label_out);
 
 /* Ring slot of latent frame `frame`; -1 if frame < 0 or the ring is invalid
- * (n_sink < 0 or n_slots <= n_sink). */
+ * (n_sink < 0 or n_slots <= n_sink).  The KV cache is indexed by latent
+ * frame (abstract: the runtime stack's faster KV indexing) and holds a
+ * limited temporal window (abstract; Table 1 row C4), so it is a ring of
+ * frame slots; the first n_sink frames stay pinned, after the attention
+ * sinks of the streaming-attention work the paper builds on (its list of
+ * cited work):
+ *   slot(f) = f                                          if f < n_sink
+ *   slot(f) = n_sink + (f - n_sink) mod (n_slots - n_sink)   otherwise. */
 int32_t ust_slot_of_frame(const ust_kv* kv, int32_t frame);
 
 /* The window of the chunk starting at frame_start, as ust_window_attn uses
- * it: frames_out[i] ascending, slots_out[i] = ust_slot_of_frame(frames[i]).
+ * it (abstract: the attention KV cache keeps a limited temporal window;
+ * Table 1 row C4: the limited attention window; Table 3: chunks of three
+ * latent frames): the prior frames f < n_sink or f >= frame_start -
+ * n_recent, each once, then the chunk's own frames; n_recent = -1 keeps
+ * every prior frame.  frames_out[i] ascending,
+ * slots_out[i] = ust_slot_of_frame(frames[i]).
  * Writes at most cap entries and the count to *n_out.
  * Errors: NULL pointers; cap too small (UST_E_SHAPE); a window frame no
  * longer held by the ring, n_recent < -1, frame_start < 0, or more than
