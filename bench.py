@@ -777,7 +777,7 @@ def main_conv(args):
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": conv_traffic(args.workload),
-            "kernel": f"conv3d_causal_kernel<{c.ci}>",
+            "kernel": f"conv3d_causal_kernel<{min(c.ci, 32)}, {c.ci}>",
             "kernel_us": round(kern_us, 2),
             "kernel_us_spread": pct(each),
             "timing": f"HIP events on the launch stream around groups of {G} back-to-back "

@@ -82,13 +82,16 @@ __device__ __forceinline__ int conv_key(int row) {
   else return (row >> 3) & 1;
 }
 
-template <int Ci>
+// CQ input channels per stage: 16 when Ci is 16, else 32 (Ci a multiple of
+// 32).  CI is Ci as a compile-time constant for the common widths (its index
+// arithmetic then folds), or 0 to take Ci from the arguments.
+template <int CQ, int CI>
 __global__ void __launch_bounds__(64 * kConvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 conv3d_causal_kernel(ConvArgs a) {
-  constexpr int CQ = Ci < 32 ? Ci : 32;       // input channels per stage
   constexpr int NCH = CQ / 8;                 // 16-byte chunks per staged row
-  constexpr int NQ = Ci / CQ;                 // channel groups
-  constexpr int NSTAGE = 9 * NQ;              // (dt, dy, channel group)
+  const int Ci = CI ? CI : a.Ci;
+  const int NQ = Ci / CQ;                     // channel groups
+  const int NSTAGE = 9 * NQ;                  // (dt, dy, channel group)
   constexpr int KS = CQ / 16;                 // k-steps per tap per stage
   constexpr int IN_EL = kConvRows * CQ;       // input block elements
   constexpr int W_EL = 3 * kConvCo * CQ;      // three taps' weights
@@ -154,9 +157,9 @@ conv3d_causal_kernel(ConvArgs a) {
           const int ew = e - IN_EL;
           const int row = ew / CQ, cp = (ew % CQ) / 8;       // row = dx * 128 + co
           const int c = cp ^ conv_key<NCH>(row);
-          const int dx = row / kConvCo, co = row - dx * kConvCo;
-          const int tap = dt * 9 + dy * 3 + dx;
-          conv_load_lds16(a.w, uint32_t((((co0 + co) * 27 + tap) * Ci + q * CQ + c * 8) * 2), dst);
+          const int dx = row / kConvCo, co = min(co0 + row - dx * kConvCo, a.Co - 1);
+          const int tap = dt * 9 + dy * 3 + dx;     // (rows past Co: clamped, never stored)
+          conv_load_lds16(a.w, uint32_t(((co * 27 + tap) * Ci + q * CQ + c * 8) * 2), dst);
         }
       }
     }
@@ -222,7 +225,8 @@ conv3d_causal_kernel(ConvArgs a) {
     if (p >= P) continue;
     uint16_t* yp = a.y + int64_t(p) * Co + co0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+      if (co0 + 32 * b >= Co) break;   // Co is a multiple of 32
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int co = 32 * b + 8 * g + 4 * half;
@@ -233,6 +237,7 @@ conv3d_causal_kernel(ConvArgs a) {
         }
         *reinterpret_cast<uint2*>(yp + co) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
+    }
   }
 }
 
@@ -240,14 +245,19 @@ conv3d_causal_kernel(ConvArgs a) {
 
 hipError_t launch_conv3d_causal(const ConvArgs& a, hipStream_t s) {
   const int64_t P = int64_t(a.T) * a.H * a.W;
-  const dim3 grid(unsigned((P + kConvPos - 1) / kConvPos), unsigned(a.Co / kConvCo));
+  const dim3 grid(unsigned((P + kConvPos - 1) / kConvPos), unsigned((a.Co + kConvCo - 1) / kConvCo));
   const dim3 block(64 * kConvWaves);
+  if (a.Co % 32 != 0) return hipErrorInvalidValue;
   switch (a.Ci) {
-    case 16: hipLaunchKernelGGL(conv3d_causal_kernel<16>, grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL(conv3d_causal_kernel<32>, grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL(conv3d_causal_kernel<64>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(conv3d_causal_kernel<128>, grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 16: hipLaunchKernelGGL((conv3d_causal_kernel<16, 16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((conv3d_causal_kernel<32, 32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((conv3d_causal_kernel<32, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((conv3d_causal_kernel<32, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((conv3d_causal_kernel<32, 256>), grid, block, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((conv3d_causal_kernel<32, 512>), grid, block, 0, s, a); break;
+    default:
+      if (a.Ci <= 0 || a.Ci % 32 != 0) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((conv3d_causal_kernel<32, 0>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

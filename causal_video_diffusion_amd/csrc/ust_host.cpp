@@ -550,9 +550,9 @@ ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, vo
     if (int64_t(T) * H * W >= (int64_t(1) << 31))
       return fail(UST_E_SHAPE, "T*H*W = %lld positions: at most 2^31 - 1",
                   static_cast<long long>(int64_t(T) * H * W));
-    if (Ci != 16 && Ci != 32 && Ci != 64 && Ci != 128)
-      return fail(UST_E_UNSUPPORTED, "Ci %d: 16, 32, 64 or 128 supported", Ci);
-    if (Co % 128 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 128 supported", Co);
+    if (Ci != 16 && Ci % 32 != 0)
+      return fail(UST_E_UNSUPPORTED, "Ci %d: 16 or a multiple of 32 supported", Ci);
+    if (Co % 32 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 32 supported", Co);
     if (int64_t(T) * H * W * std::max(Ci, Co) >= (int64_t(1) << 30) ||
         int64_t(Co) * 27 * Ci >= (int64_t(1) << 30))
       return fail(UST_E_SHAPE, "tensors too large for 32-bit byte offsets");

@@ -319,9 +319,9 @@ ust_status ust_flow_step(const float* x, const void* v, const float* noise, floa
  * Arithmetic: bf16 MFMA with fp32 accumulation, the output rounded to bf16
  * once (bias added in fp32).
  * Errors: NULL x, w or y (UST_E_NULL); a non-positive size, or x, y or w
- * of 2^30 elements or more (UST_E_SHAPE); Ci not 16, 32, 64 or 128, or Co
- * not a multiple of 128 (UST_E_UNSUPPORTED); a pointer not 16-byte aligned
- * (UST_E_ALIGN). */
+ * of 2^30 elements or more (UST_E_SHAPE); Ci neither 16 nor a multiple of
+ * 32, or Co not a multiple of 32 (UST_E_UNSUPPORTED); a pointer not 16-byte
+ * aligned (UST_E_ALIGN). */
 ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, void* y,
                              int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
                              hipStream_t stream);

@@ -81,3 +81,39 @@ def test_conv3d_deterministic_and_causal():
     y3 = _conv_gpu(c, x2, w, b)
     assert np.array_equal(y1[:2], y3[:2])
     assert not np.array_equal(y1[2:], y3[2:])
+
+
+# input widths 16 and 32 .. 512 (multiples of 32, including the 96 / 192 /
+# 384 of some decoders), output widths that are multiples of 32 but not of
+# the 128-channel tile, and degenerate and ragged grids: a single position,
+# H = 1, W = 1, T = 1, fewer positions than one 512-position tile, a ragged
+# last tile
+_EDGE = [
+    (45, 1, 1, 1, 32, 128),
+    (46, 2, 1, 37, 32, 128),
+    (47, 3, 7, 1, 128, 256),
+    (48, 6, 11, 17, 32, 384),
+    (49, 1, 30, 52, 64, 128),
+    (50, 9, 6, 10, 16, 128),
+    (51, 4, 5, 33, 128, 128),
+    (52, 3, 8, 12, 96, 96),
+    (53, 2, 9, 14, 192, 224),
+    (54, 3, 6, 11, 384, 384),
+    (55, 2, 5, 7, 512, 160),
+    (56, 4, 6, 9, 256, 32),
+]
+
+
+@pytest.mark.parametrize("wid,T,H,W,ci,co", _EDGE)
+def test_conv3d_edge_shapes(wid, T, H, W, ci, co):
+    c = wl.ConvWorkload(wid=wid, name=f"conv_edge{wid}", T=T, H=H, W=W, ci=ci, co=co)
+    print(f"[conv3d edge {T}x{H}x{W}, {ci} -> {co}]", flush=True)
+    x, w, b = wl.conv_tensors(c)
+    got = wl.bf16_bits_to_f64(_conv_gpu(c, x, w, b))
+    ref = O.conv3d_causal(wl.bf16_bits_to_f64(x), wl.bf16_bits_to_f64(w), b.astype(np.float64))
+    assert np.isfinite(got).all()
+    d = got - ref
+    ma = float(np.abs(d).max())
+    rl = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    print(f"  max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert ma <= 2e-2 and rl <= 1e-2

@@ -187,7 +187,9 @@ def test_compute_entry_points_reject_bad_arguments(lib):
                 None)[0] == "UST_E_SHAPE"
     assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 48, 128,
                 None)[0] == "UST_E_UNSUPPORTED"
-    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 16, 96,
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 24, 128,
+                None)[0] == "UST_E_UNSUPPORTED"
+    assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2, 3, 4, 16, 100,
                 None)[0] == "UST_E_UNSUPPORTED"
     assert _raw(lib, "ust_conv3d_causal", fake, fake + 8, None, fake, 2, 3, 4, 16, 128,
                 None)[0] == "UST_E_ALIGN"
