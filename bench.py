@@ -335,25 +335,34 @@ def main():
     def flush_read():
         torch.sum(flush, dim=0, out=fsum)
 
-    def timed(with_append):
+    def timed(op):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(20):
             flush_read()
-            if with_append:
-                B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0)
+            if op is not None:
+                op()
         e1.record(stream)
         torch.cuda.synchronize()
         return 1000.0 * e0.elapsed_time(e1)
 
-    timed(True)
-    cold_each = []
-    for _ in range(5):
-        pair_us, flush_us = timed(True), timed(False)
-        cold_each.append((pair_us - flush_us) / 20)
-    del flush
-    stage["rope_k_append_cold_us"] = float(np.median(cold_each))
+    def cold_us(op):
+        timed(op)
+        each = []
+        for _ in range(5):
+            pair_us, flush_us = timed(op), timed(None)
+            each.append((pair_us - flush_us) / 20)
+        return float(np.median(each))
+
+    stage["rope_k_append_cold_us"] = cold_us(
+        lambda: B.ust_kv_append(g, ring.abi, k, bufs.v, table.cos, table.sin, w.n_tab_frames, F0))
+    # the same measurement for a plain device copy of the append's K and V
+    # (read once, written once): what a cold launch of this size reaches
+    csrc = torch.empty(2 * w.n_q * w.hidden, dtype=torch.bfloat16, device="cuda").normal_()
+    cdst = torch.empty_like(csrc)
+    stage["copy_same_bytes_cold_us"] = cold_us(lambda: cdst.copy_(csrc))
+    del flush, csrc, cdst
     attn_tflops = flops / (attn_us * 1e-6) / 1e12
     append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
     lowrank_flops = 2 * 2.0 * w.n_q * w.hidden * w.rank
@@ -404,7 +413,9 @@ def main():
                        "(no event overhead; inputs warm); rope_k_append_cold_us: 20 "
                        "(512 MiB read, append) pairs minus 20 reads alone, per append, "
                        "median of 5 (no event between a read and its append); the 60% "
-                       "HBM target is compared with this cold figure",
+                       "HBM target is compared with this cold figure; copy_same_bytes_cold_us: "
+                       "the same measurement for a plain device copy of the append's K and V "
+                       "(28.8 MB read, 28.8 MB written), what a cold launch of that size reaches",
         "stages": {
             "rope_k_append_GBs": round(append_bytes / (stage["rope_k_append_us"] * 1e-6) / 1e9, 1),
             "rope_k_append_hbm_frac": round(append_bytes / (stage["rope_k_append_us"] * 1e-6)
@@ -413,6 +424,8 @@ def main():
                 append_bytes / (stage["rope_k_append_batched_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "rope_k_append_cold_hbm_frac": round(append_bytes / (stage["rope_k_append_cold_us"]
                                                                  * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "copy_same_bytes_cold_hbm_frac": round(4.0 * w.n_q * w.hidden * 2 / (
+                stage["copy_same_bytes_cold_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "lowrank_v_o_TFLOPs": round(lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"])
                                                          * 1e-6) / 1e12, 1),
         },
