@@ -375,11 +375,14 @@ def rne_bf16(x: np.ndarray) -> np.ndarray:
 # [Cout][3][3][3][Cin] (time, row, column offsets), bias [Cout].
 
 def conv3d_causal(x: np.ndarray, w: np.ndarray,
-                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+                  bias: Optional[np.ndarray] = None,
+                  history: Optional[np.ndarray] = None) -> np.ndarray:
     """out[t, y, x, o] = bias[o] + sum over dt, dy, dx, i of
     w[o, dt, dy, dx, i] * x[t + dt - 2, y + dy - 1, x + dx - 1, i], with x
-    zero outside its frames, rows and columns.  fp64; one matrix product per
-    kernel tap over the zero-padded input."""
+    zero outside its rows and columns, and before frame 0 zero, or, given
+    `history` [2, H, W, Ci], the two frames that precede frame 0 (the last
+    input frames of the previous chunk when a clip is decoded chunk by
+    chunk).  fp64; one matrix product per kernel tap over the padded input."""
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     T, H, W, Ci = x.shape
@@ -387,6 +390,10 @@ def conv3d_causal(x: np.ndarray, w: np.ndarray,
     assert w.shape == (Co, 3, 3, 3, Ci)
     xp = np.zeros((T + 2, H + 2, W + 2, Ci))
     xp[2:, 1:H + 1, 1:W + 1] = x
+    if history is not None:
+        history = np.asarray(history, dtype=np.float64)
+        assert history.shape == (2, H, W, Ci)
+        xp[:2, 1:H + 1, 1:W + 1] = history
     out = np.zeros((T, H, W, Co))
     for dt in range(3):
         for dy in range(3):

@@ -624,3 +624,32 @@ def test_conv3d_equals_torch_conv3d_on_padded_input():
     wt = torch.from_numpy(w).permute(0, 4, 1, 2, 3)               # [Co][Ci][3][3][3]
     ref = F.conv3d(xt, wt, torch.from_numpy(b))[0].permute(1, 2, 3, 0).numpy()
     assert np.max(np.abs(O.conv3d_causal(x, w, b) - ref)) < 1e-11
+
+
+def test_conv3d_history_is_the_clip_before_the_chunk():
+    """Decoding chunk by chunk with the previous chunk's last two input
+    frames as history reproduces the whole clip (chunks of three frames,
+    zero history for the first), and the history path equals the scalar
+    brute force run over history and chunk together, keeping the outputs of
+    the chunk's own frames."""
+    x, w, b = _conv_inputs(9, 3, 4, 5, 6, 5)
+    whole = O.conv3d_causal(x, w, b)
+    parts = []
+    for c in range(3):
+        hist = np.zeros((2,) + x.shape[1:])
+        lo = 3 * c - 2
+        for k in range(2):
+            if lo + k >= 0:
+                hist[k] = x[lo + k]
+        parts.append(O.conv3d_causal(x[3 * c:3 * c + 3], w, b, history=hist))
+    assert np.max(np.abs(np.concatenate(parts) - whole)) < 1e-12
+    # zero history is no history
+    assert np.array_equal(O.conv3d_causal(x, w, b, history=np.zeros((2,) + x.shape[1:])),
+                          O.conv3d_causal(x, w, b))
+    # random history against brute force over [history, chunk]
+    hist = np.random.default_rng(6).standard_normal((2,) + x.shape[1:])
+    xs = x[:3]
+    got = O.conv3d_causal(xs, w, b, history=hist)
+    ext = np.concatenate([hist, xs])
+    ref = np.array(brute.conv3d_causal(ext.tolist(), w.tolist(), b.tolist()))[2:]
+    assert np.max(np.abs(got - ref)) < 1e-12
