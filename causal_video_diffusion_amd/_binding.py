@@ -23,7 +23,8 @@ EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
            "ust_window_attn", "ust_window_attn_work_bytes", "ust_window_attn_split",
            "ust_qkv_append", "ust_lowrank_proj", "ust_flow_step", "ust_slot_of_frame",
            "ust_window_plan", "ust_sigma_schedule", "ust_status_str", "ust_last_error",
-           "ust_calib_mfma_bf16", "ust_lowrank_proj_static", "ust_conv3d_causal")
+           "ust_calib_mfma_bf16", "ust_lowrank_proj_static", "ust_conv3d_causal",
+           "ust_conv3d_causal_stream")
 
 
 class UstError(RuntimeError):
@@ -73,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_lowrank_proj_static": (I32, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_conv3d_causal": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
+        "ust_conv3d_causal_stream": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
         "ust_flow_step": (I32, [P, P, P, F32, F32, P, P, ctypes.c_int64, P]),
         "ust_sigma_schedule": (I32, [IP, I32, F64, I32, ctypes.POINTER(F64),
                                      ctypes.POINTER(F64)]),
@@ -196,6 +198,12 @@ def ust_conv3d_causal(x, w, bias, y, T: int, H: int, W: int, Ci: int, Co: int,
                       stream=None) -> None:
     _check(load().ust_conv3d_causal(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), T, H, W, Ci, Co,
                                     _stream(stream)))
+
+
+def ust_conv3d_causal_stream(x, w, bias, y, T: int, H: int, W: int, Ci: int, Co: int,
+                             stream=None) -> None:
+    _check(load().ust_conv3d_causal_stream(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), T, H, W, Ci,
+                                           Co, _stream(stream)))
 
 
 def ust_flow_step(x, v, noise, sigma: float, sigma_next: float, x0_out, x_next, n: int,

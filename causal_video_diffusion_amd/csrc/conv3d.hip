@@ -116,6 +116,10 @@ conv3d_causal_kernel(ConvArgs a) {
   const int co0 = blockIdx.y * kConvCo;
   const int p0 = tile * kConvPos;
 
+  // frames before frame 0: zero padding, or the two history frames at the
+  // start of x (then input position p lives at x[p + 2 H W])
+  const int t_lo = a.hist ? -2 : 0;
+  const int pos_lo = t_lo * HW;
   // the taps each of this lane's two positions may read
   uint32_t tapmask[2];
 #pragma unroll
@@ -127,7 +131,7 @@ conv3d_causal_kernel(ConvArgs a) {
 #pragma unroll
       for (int tap = 0; tap < 27; ++tap) {
         const int t2 = pt + tap / 9 - 2, y2 = py + (tap / 3) % 3 - 1, x2 = px + tap % 3 - 1;
-        if (t2 >= 0 && y2 >= 0 && y2 < a.H && x2 >= 0 && x2 < a.W) m |= 1u << tap;
+        if (t2 >= t_lo && y2 >= 0 && y2 < a.H && x2 >= 0 && x2 < a.W) m |= 1u << tap;
       }
     }
     tapmask[pb] = m;
@@ -151,8 +155,8 @@ conv3d_causal_kernel(ConvArgs a) {
           const int row = e / CQ, cp = (e % CQ) / 8;
           const int c = cp ^ conv_key<NCH>(row);
           int pos = p0 + shift + row;
-          pos = pos < 0 ? 0 : (pos >= P ? P - 1 : pos);      // clamped; such taps are masked
-          conv_load_lds16(a.x, uint32_t((pos * Ci + q * CQ + c * 8) * 2), dst);
+          pos = pos < pos_lo ? pos_lo : (pos >= P ? P - 1 : pos);  // clamped; such taps are masked
+          conv_load_lds16(a.x, uint32_t(((pos - pos_lo) * Ci + q * CQ + c * 8) * 2), dst);
         } else {
           const int ew = e - IN_EL;
           const int row = ew / CQ, cp = (ew % CQ) / 8;       // row = dx * 128 + co

@@ -464,6 +464,35 @@ ust_status lowrank_proj(const void* x, const void* a, const void* b, const void*
   }
 }
 
+// ust_conv3d_causal (hist false) and ust_conv3d_causal_stream (x starts
+// with two history frames)
+ust_status conv3d(const void* x, const void* w, const float* bias, void* y, int32_t T, int32_t H,
+                  int32_t W, int32_t Ci, int32_t Co, bool hist, hipStream_t stream) {
+  try {
+    if (!x || !w || !y) return fail(UST_E_NULL, "x, w or y is NULL");
+    if (T <= 0 || H <= 0 || W <= 0 || Ci <= 0 || Co <= 0)
+      return fail(UST_E_SHAPE, "sizes must be positive (T=%d H=%d W=%d Ci=%d Co=%d)", T, H, W,
+                  Ci, Co);
+    const int64_t tx = int64_t(T) + (hist ? 2 : 0);   // frames of x
+    if (tx * H * W >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "%lld input positions: at most 2^31 - 1",
+                  static_cast<long long>(tx * H * W));
+    if (Ci != 16 && Ci % 32 != 0)
+      return fail(UST_E_UNSUPPORTED, "Ci %d: 16 or a multiple of 32 supported", Ci);
+    if (Co % 32 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 32 supported", Co);
+    if (tx * H * W * Ci >= (int64_t(1) << 30) || int64_t(T) * H * W * Co >= (int64_t(1) << 30) ||
+        int64_t(Co) * 27 * Ci >= (int64_t(1) << 30))
+      return fail(UST_E_SHAPE, "tensors too large for 32-bit byte offsets");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    ust::ConvArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
+                    static_cast<uint16_t*>(y), T, H, W, Ci, Co, hist ? 1 : 0};
+    return hip_status(ust::launch_conv3d_causal(a, stream), "conv3d_causal launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -542,28 +571,13 @@ ust_status ust_calib_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out,
 ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, void* y,
                              int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
                              hipStream_t stream) {
-  try {
-    if (!x || !w || !y) return fail(UST_E_NULL, "x, w or y is NULL");
-    if (T <= 0 || H <= 0 || W <= 0 || Ci <= 0 || Co <= 0)
-      return fail(UST_E_SHAPE, "sizes must be positive (T=%d H=%d W=%d Ci=%d Co=%d)", T, H, W,
-                  Ci, Co);
-    if (int64_t(T) * H * W >= (int64_t(1) << 31))
-      return fail(UST_E_SHAPE, "T*H*W = %lld positions: at most 2^31 - 1",
-                  static_cast<long long>(int64_t(T) * H * W));
-    if (Ci != 16 && Ci % 32 != 0)
-      return fail(UST_E_UNSUPPORTED, "Ci %d: 16 or a multiple of 32 supported", Ci);
-    if (Co % 32 != 0) return fail(UST_E_UNSUPPORTED, "Co %d: a multiple of 32 supported", Co);
-    if (int64_t(T) * H * W * std::max(Ci, Co) >= (int64_t(1) << 30) ||
-        int64_t(Co) * 27 * Ci >= (int64_t(1) << 30))
-      return fail(UST_E_SHAPE, "tensors too large for 32-bit byte offsets");
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
-      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
-    ust::ConvArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
-                    static_cast<uint16_t*>(y), T, H, W, Ci, Co};
-    return hip_status(ust::launch_conv3d_causal(a, stream), "conv3d_causal launch");
-  } catch (...) {
-    return fail(UST_E_HIP, "internal error");
-  }
+  return conv3d(x, w, bias, y, T, H, W, Ci, Co, false, stream);
+}
+
+ust_status ust_conv3d_causal_stream(const void* x, const void* w, const float* bias, void* y,
+                                    int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
+                                    hipStream_t stream) {
+  return conv3d(x, w, bias, y, T, H, W, Ci, Co, true, stream);
 }
 
 }  // extern "C"

@@ -97,6 +97,7 @@ struct ConvArgs {
   const float* bias;         // [Co] or nullptr
   uint16_t* y;               // [T][H][W][Co] bf16
   int32_t T, H, W, Ci, Co;
+  int32_t hist;              // 1: x starts with two history frames ([T+2][H][W][Ci])
 };
 
 hipError_t launch_rope_table(const RopeTableArgs& a, hipStream_t s);

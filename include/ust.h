@@ -29,6 +29,8 @@
  *   ust_sigma_schedule    the sampler's noise levels (host only; Table 4)
  *   ust_conv3d_causal     the decoder's causal 3-D convolution, channels last
  *                         (abstract: VAE decoding runtime stack; Table 3)
+ *   ust_conv3d_causal_stream  the same for a clip decoded chunk by chunk, two
+ *                         history frames in place of the zero padding
  *
  * Conventions (all entry points):
  *  - Device pointers are caller-owned.  The library never allocates, frees
@@ -325,6 +327,21 @@ ust_status ust_flow_step(const float* x, const void* v, const float* noise, floa
 ust_status ust_conv3d_causal(const void* x, const void* w, const float* bias, void* y,
                              int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
                              hipStream_t stream);
+
+/* The same convolution for a clip decoded chunk by chunk (the pages'
+ * generation is streamed in chunks of three latent frames, Table 3): x
+ * holds two history frames, the last two input frames of the previous
+ * chunk (zeros before a clip's first chunk), then the chunk's T frames, and
+ * the history takes the place of the zero padding in front:
+ *   y[t] = the convolution above at frame t + 2 of x, for t = 0 .. T-1.
+ *   x:    bf16 [T + 2][H][W][Ci] (channels last), read.
+ *   y:    bf16 [T][H][W][Co], written; must not overlap x.
+ * The arithmetic is that of ust_conv3d_causal, so a clip decoded in chunks
+ * equals the whole-clip call bit for bit.  Errors: as ust_conv3d_causal,
+ * with (T + 2) H W Ci the size of x. */
+ust_status ust_conv3d_causal_stream(const void* x, const void* w, const float* bias, void* y,
+                                    int32_t T, int32_t H, int32_t W, int32_t Ci, int32_t Co,
+                                    hipStream_t stream);
 
 /* ---- host-only helpers (no GPU needed) ---- */
 

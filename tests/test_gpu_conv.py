@@ -117,3 +117,59 @@ def test_conv3d_edge_shapes(wid, T, H, W, ci, co):
     rl = float(np.linalg.norm(d) / np.linalg.norm(ref))
     print(f"  max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
     assert ma <= 2e-2 and rl <= 1e-2
+
+
+def _stream_chunks(c, x_dev, w_dev, b_dev, chunk=3):
+    """The clip through ust_conv3d_causal_stream, chunk by chunk: each call
+    gets the previous chunk's last two input frames (zeros first) and the
+    chunk's frames, contiguous."""
+    outs = []
+    zeros = torch.zeros((2, c.H, c.W, c.ci), dtype=torch.bfloat16, device="cuda")
+    for t0 in range(0, c.T, chunk):
+        n = min(chunk, c.T - t0)
+        hist = zeros if t0 == 0 else (x_dev[t0 - 2:t0] if t0 >= 2 else
+                                      torch.cat([zeros[:2 - t0], x_dev[:t0]]))
+        x_ext = torch.cat([hist, x_dev[t0:t0 + n]]).contiguous()
+        y = torch.full((n, c.H, c.W, c.co), float("nan"), dtype=torch.bfloat16, device="cuda")
+        B.ust_conv3d_causal_stream(x_ext, w_dev, b_dev, y, n, c.H, c.W, c.ci, c.co)
+        outs.append(y)
+    torch.cuda.synchronize()
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("name", ["conv_mid", "vae_conv"])
+def test_conv3d_stream_chunks_equal_whole_clip(name):
+    """Decoding the clip in chunks of three latent frames with the two
+    history frames reproduces the whole-clip convolution bit for bit."""
+    c = wl.CONV_ALL[name]
+    print(f"[conv3d stream {name}: {c.T}x{c.H}x{c.W}, {c.ci} -> {c.co}]", flush=True)
+    x, w, b = wl.conv_tensors(c)
+    xd, wd, bd = P.to_device_bf16(x), P.to_device_bf16(w), torch.from_numpy(b).cuda()
+    whole = torch.empty((c.T, c.H, c.W, c.co), dtype=torch.bfloat16, device="cuda")
+    B.ust_conv3d_causal(xd, wd, bd, whole, c.T, c.H, c.W, c.ci, c.co)
+    got = _stream_chunks(c, xd, wd, bd)
+    assert torch.equal(got.view(torch.int16), whole.view(torch.int16))
+
+
+@pytest.mark.parametrize("wid,T,H,W,ci,co", [(57, 3, 9, 13, 64, 128), (58, 1, 6, 11, 16, 96),
+                                             (59, 2, 5, 7, 192, 160)])
+def test_conv3d_stream_random_history_matches_oracle(wid, T, H, W, ci, co):
+    """Random history frames (not a previous chunk of the same clip) against
+    the oracle's history form."""
+    c = wl.ConvWorkload(wid=wid, name=f"conv_hist{wid}", T=T, H=H, W=W, ci=ci, co=co)
+    x, w, b = wl.conv_tensors(c)
+    hist = wl.f32_to_bf16_bits(
+        np.random.default_rng(wid).standard_normal((2, H, W, ci)).astype(np.float32))
+    x_ext = np.concatenate([hist, x])
+    y = torch.full((T, H, W, co), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.ust_conv3d_causal_stream(P.to_device_bf16(x_ext), P.to_device_bf16(w),
+                               torch.from_numpy(b).cuda(), y, T, H, W, ci, co)
+    torch.cuda.synchronize()
+    got = wl.bf16_bits_to_f64(P.from_device_bf16(y))
+    ref = O.conv3d_causal(wl.bf16_bits_to_f64(x), wl.bf16_bits_to_f64(w), b.astype(np.float64),
+                          history=wl.bf16_bits_to_f64(hist))
+    d = got - ref
+    ma = float(np.abs(d).max())
+    rl = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    print(f"  history {T}x{H}x{W} {ci}->{co}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert np.isfinite(got).all() and ma <= 2e-2 and rl <= 1e-2

@@ -40,7 +40,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 18
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -194,6 +194,14 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     assert _raw(lib, "ust_conv3d_causal", fake, fake + 8, None, fake, 2, 3, 4, 16, 128,
                 None)[0] == "UST_E_ALIGN"
     assert _raw(lib, "ust_conv3d_causal", fake, fake, None, fake, 2048, 1024, 1024, 16, 128,
+                None)[0] == "UST_E_SHAPE"
+    # the streaming form: x holds T + 2 frames
+    assert _raw(lib, "ust_conv3d_causal_stream", None, fake, None, fake, 2, 3, 4, 16, 128,
+                None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_conv3d_causal_stream", fake, fake, None, fake, 2, 3, 4, 24, 128,
+                None)[0] == "UST_E_UNSUPPORTED"
+    # 63 x 512 x 1024 x 32 elements fit under 2^30, the 65 frames of x do not
+    assert _raw(lib, "ust_conv3d_causal_stream", fake, fake, None, fake, 63, 512, 1024, 32, 32,
                 None)[0] == "UST_E_SHAPE"
     # frames outside the table
     assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 21, 19, None)[0] == "UST_E_RANGE"
