@@ -52,7 +52,7 @@ ATTN_TRAFFIC = {
 # the decoder convolution, per workload, same scaling and keying
 CONV_SOURCES = ("conv3d.hip", "ust_device.h")
 CONV_TRAFFIC = {
-    "vae_conv": {"src_sha16": "4906a20a10c95840", "bytes": (2 * 62823 + 32776) * 1024},
+    "vae_conv": {"src_sha16": "047f294e4bbd3dcf", "bytes": (2 * 62823 + 32776) * 1024},
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7

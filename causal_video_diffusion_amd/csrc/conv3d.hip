@@ -2,7 +2,9 @@
 // decoder runs with an optimised memory layout, precision and convolution
 // kernels; Table 3: the decoder turns 21 latent frames of 16 x 60 x 104 into
 // 81 frames of 832 x 480).  Output frame t reads input frames t-2 .. t (zero
-// before the first), rows and columns with zero padding 1, stride 1.
+// before the first; in the streaming form, for a clip decoded chunk by
+// chunk, x starts with two history frames that take the padding's place),
+// rows and columns with zero padding 1, stride 1.
 //
 // Layout and precision: activations channels last [T][H][W][C] bf16, weights
 // [Cout][3][3][3][Cin] bf16, bias fp32, fp32 accumulation, bf16 out.  With
@@ -25,7 +27,9 @@
 //    frame, columns that would wrap into the next row) are zeroed per
 //    position after the fragment read.
 //  * Each lane ends with 4 consecutive output channels of one position per
-//    register group: 8-byte stores.
+//    register group: 8-byte stores.  Co is a multiple of 32: in a last,
+//    partly empty 128-channel tile the missing weight rows load a clamped
+//    (finite) row and their outputs are not stored.
 
 #include <type_traits>
 
