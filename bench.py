@@ -522,6 +522,44 @@ def main_fused(args):
     names = ["qkv_proj_rope_k_append_us", "window_attn_us", "o_proj_us"]
     stage = {n: round(1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs])), 2)
              for i, n in enumerate(names)}
+
+    # The fused projection against the separate path it replaces (three dense
+    # projections, then ust_kv_append rotating K and appending K and V into a
+    # ring of its own), each launched 20 times back to back with no event in
+    # between, alternating, 5 rounds; per call, median over the rounds.
+    HD = w.n_heads * w.head_dim
+    ring_sep = P.Ring(g, w.n_slots, w.n_sink, fill_bits=0x7FC1)
+    ysep = [torch.empty((w.n_q, HD), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+
+    def fused_only():
+        B.ust_qkv_append(g, ring.abi, x, w_qkv, w.hidden, table.cos, table.sin, w.n_tab_frames,
+                         F0, qbuf)
+
+    def separate_only():
+        for i in range(3):
+            B.ust_lowrank_proj(x, w_qkv[i * HD:(i + 1) * HD], None, None, None, ysep[i], w.n_q,
+                               w.hidden, HD, HD)
+        B.ust_kv_append(g, ring_sep.abi, ysep[1], ysep[2], table.cos, table.sin, w.n_tab_frames,
+                        F0)
+
+    def back_to_back(fn, reps=20):
+        for _ in range(3):
+            fn()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(reps):
+            fn()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * b0.elapsed_time(b1) / reps
+
+    pair = {"fused": [], "separate": []}
+    for _ in range(5):
+        pair["fused"].append(back_to_back(fused_only))
+        pair["separate"].append(back_to_back(separate_only))
+    stage["qkv_fused_back_to_back_us"] = round(float(np.median(pair["fused"])), 2)
+    stage["qkv_separate_back_to_back_us"] = round(float(np.median(pair["separate"])), 2)
     attn_tflops = flops / (stage["window_attn_us"] * 1e-6) / 1e12
     qkv_flops = 3 * 2.0 * w.n_q * w.hidden * w.n_heads * w.head_dim
     o_flops = 2.0 * w.n_q * w.hidden * w.hidden
@@ -559,9 +597,15 @@ def main_fused(args):
         "stages": {
             "qkv_TFLOPs": round(qkv_flops / (stage["qkv_proj_rope_k_append_us"] * 1e-6) / 1e12, 1),
             "o_proj_TFLOPs": round(o_flops / (stage["o_proj_us"] * 1e-6) / 1e12, 1),
+            "qkv_fused_gain_vs_separate": round(
+                stage["qkv_separate_back_to_back_us"] / stage["qkv_fused_back_to_back_us"] - 1.0, 4),
         },
         "stages_note": "separate untimed pass with events between the stages (each event "
-                       "adds ~2-3 us; stage times include launch gaps)",
+                       "adds ~2-3 us; stage times include launch gaps); "
+                       "qkv_fused_back_to_back_us / qkv_separate_back_to_back_us: the fused "
+                       "projection + append, and the three dense projections + ust_kv_append it "
+                       "replaces, each 20 times back to back, alternating, median of 5 rounds, "
+                       "per call; qkv_fused_gain_vs_separate = separate / fused - 1",
     }
     print(json.dumps(result), flush=True)
 

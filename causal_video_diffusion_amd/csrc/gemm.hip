@@ -346,36 +346,12 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   }
 
   // which output of the fused projection this tile is (0 Q, 1 K, 2 V) and
-  // its head; K is rotated in fp32 before its one bf16 rounding
+  // its head
   int which = 0, h = 0;
   if constexpr (QKV) {
     const int HD = e.H * BN;
     which = n0 / HD;
     h = (n0 - which * HD) / BN;
-    if (which == 1) {
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int col = wn * 32 * NB + 32 * i + 8 * qq + 4 * half;   // dims col .. col+3
-#pragma unroll
-          for (int j = 0; j < MB; ++j) {
-            const int m = m0 + wm * 32 * MB + 32 * j + l32;
-            if (m < g.M) {
-              const int64_t trow = (int64_t(e.frame_start) * e.T + m) * (BN / 2) + col / 2;
-              const float2 cs = *reinterpret_cast<const float2*>(e.cos_tab + trow);
-              const float2 sn = *reinterpret_cast<const float2*>(e.sin_tab + trow);
-              f32x16& a4 = acc[i][j];
-              const float x0 = a4[4 * qq], x1 = a4[4 * qq + 1];
-              const float x2 = a4[4 * qq + 2], x3 = a4[4 * qq + 3];
-              a4[4 * qq] = x0 * cs.x - x1 * sn.x;
-              a4[4 * qq + 1] = x0 * sn.x + x1 * cs.x;
-              a4[4 * qq + 2] = x2 * cs.y - x3 * sn.y;
-              a4[4 * qq + 3] = x2 * sn.y + x3 * cs.y;
-            }
-          }
-        }
-    }
   }
 
   // epilogue: bias, bf16, staged through LDS so each row leaves in 16-byte
@@ -385,6 +361,13 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   constexpr int ESV = BN + 2;
   static_assert(BM * ESV <= STAGES * STAGE, "V staging tile fits in the ring");
   const int es = QKV && which == 2 ? ESV : ES;
+  // K tiles stage the fp32 product (rows of ESF floats: the 16-byte writes of
+  // 16 consecutive rows start 4 banks apart); the rotation and the one bf16
+  // rounding happen on the way out, where the table rows are read coalesced
+  constexpr int ESF = BN + 4;
+  static_assert(BM * ESF * 2 <= STAGES * STAGE, "fp32 K staging tile fits in the ring");
+  float* const ldsf = reinterpret_cast<float*>(lds);
+  const bool kf32 = QKV && which == 1;
   wait_vm_lds<0>();
   barrier();
 #pragma unroll
@@ -402,6 +385,11 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
       for (int j = 0; j < MB; ++j) {
         const int row = wm * 32 * MB + 32 * j + l32;
         const f32x16& a4 = acc[i][j];
+        if (kf32) {
+          *reinterpret_cast<float4*>(ldsf + row * ESF + col) =
+              make_float4(a4[4 * qq], a4[4 * qq + 1], a4[4 * qq + 2], a4[4 * qq + 3]);
+          continue;
+        }
         const uint32_t lo = pack_bf16x2(a4[4 * qq] + bv[0], a4[4 * qq + 1] + bv[1]);
         const uint32_t hi = pack_bf16x2(a4[4 * qq + 2] + bv[2], a4[4 * qq + 3] + bv[3]);
         if (es == ES) {
@@ -425,22 +413,57 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
         *reinterpret_cast<uint4*>(g.y + int64_t(m) * g.N + n) =
             *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
     }
-  } else if (which < 2) {
-    // Q rows to q_out, K rows into the ring slot of the token's frame
+  } else if (which == 0) {
+    // Q rows to q_out
+#pragma unroll
+    for (int it = 0; it < BM * CPR / NT; ++it) {
+      const int idx = tid + NT * it;
+      const int rrow = idx / CPR, c = idx % CPR;
+      const int m = m0 + rrow;
+      if (m < g.M)
+        *reinterpret_cast<uint4*>(e.q_out + (int64_t(m) * e.H + h) * BN + c * 8) =
+            *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
+    }
+  } else if (which == 1) {
+    // K rows: 8 dims (4 rotation pairs) per piece, rotated in fp32 with the
+    // token's table row (consecutive lanes read consecutive 16 bytes of it),
+    // rounded once, into the ring slot of the token's frame
 #pragma unroll
     for (int it = 0; it < BM * CPR / NT; ++it) {
       const int idx = tid + NT * it;
       const int rrow = idx / CPR, c = idx % CPR;
       const int m = m0 + rrow;
       if (m < g.M) {
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + rrow * ES + c * 8);
-        if (which == 0) {
-          *reinterpret_cast<uint4*>(e.q_out + (int64_t(m) * e.H + h) * BN + c * 8) = v;
-        } else {
-          const int fi = m / e.T, t = m - fi * e.T;
-          *reinterpret_cast<uint4*>(
-              e.k_cache + ((int64_t(e.chunk_slot[fi]) * e.H + h) * e.T + t) * BN + c * 8) = v;
+        const float4 xa = *reinterpret_cast<const float4*>(ldsf + rrow * ESF + c * 8);
+        const float4 xb = *reinterpret_cast<const float4*>(ldsf + rrow * ESF + c * 8 + 4);
+        const int64_t trow = (int64_t(e.frame_start) * e.T + m) * (BN / 2) + c * 4;
+        const float4 cs = *reinterpret_cast<const float4*>(e.cos_tab + trow);
+        const float4 sn = *reinterpret_cast<const float4*>(e.sin_tab + trow);
+        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
+        const float s4[4] = {sn.x, sn.y, sn.z, sn.w};
+        float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (g.bias) {
+          const uint4 b8 = *reinterpret_cast<const uint4*>(g.bias + n0 + c * 8);
+          const uint32_t bw[4] = {b8.x, b8.y, b8.z, b8.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            bv[2 * k] = bf16_lo(bw[k]);
+            bv[2 * k + 1] = bf16_hi(bw[k]);
+          }
         }
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x0 = x[2 * k], x1 = x[2 * k + 1];
+          const float r0 = x0 * c4[k] - x1 * s4[k];
+          const float r1 = x0 * s4[k] + x1 * c4[k];
+          o[k] = pack_bf16x2(r0 + bv[2 * k], r1 + bv[2 * k + 1]);
+        }
+        const int fi = m / e.T, t = m - fi * e.T;
+        *reinterpret_cast<uint4*>(
+            e.k_cache + ((int64_t(e.chunk_slot[fi]) * e.H + h) * e.T + t) * BN + c * 8) =
+            make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
   } else {
