@@ -23,6 +23,9 @@
 //    weights go global -> LDS (global_load_lds, coalesced 64-byte rows,
 //    16-byte chunks XOR-swizzled so operand reads hit distinct banks),
 //    double-buffered: stage s+1 loads while stage s computes.
+//  * Within a stage the operand fragments of the next (tap, 16 channels)
+//    step are read from LDS between the current step's MFMAs, so the matrix
+//    pipe does not wait on LDS latency at each step.
 //  * Taps that leave the input (frames before the first, rows off the
 //    frame, columns that would wrap into the next row) are zeroed per
 //    position after the fragment read.
@@ -189,31 +192,45 @@ conv3d_causal_kernel(ConvArgs a) {
     const int dtdy = s / NQ;
     const uint16_t* X = lds + buf * BUF;
     const uint16_t* Wt = X + IN_EL;
+    // fragments of two steps: step j's feed its MFMAs while step j+1's are read
+    bf16x8 bfr[2][2], afr[2][4];
+    auto rd = [&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int dx = j / KS, k = j % KS, PAR = j & 1;
+      const int tap = dtdy * 3 + dx;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        const int row = wave * 64 + pb * 32 + l32 + dx;
+        uint4 v = *reinterpret_cast<const uint4*>(X + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8));
+        if (!((tapmask[pb] >> tap) & 1u)) v = make_uint4(0, 0, 0, 0);
+        bfr[PAR][pb] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int row = dx * kConvCo + 32 * b + l32;
+        afr[PAR][b] = as_bf16x8(*reinterpret_cast<const uint4*>(Wt + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8)));
+      }
+    };
+    rd(std::integral_constant<int, 0>{});
     static_for<0, NSTEP>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      constexpr int dx = j / KS, k = j % KS;
-      const int tap = dtdy * 3 + dx;
+      constexpr int PAR = j & 1;
       if (next)
         issue(s + 1, buf ^ 1, std::integral_constant<int, j * LPW / NSTEP>{},
               std::integral_constant<int, (j + 1) * LPW / NSTEP>{});
-      {
-        bf16x8 bfr[2], afr[4];
+      if constexpr (j + 1 < NSTEP) rd(std::integral_constant<int, j + 1>{});
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
-          const int row = wave * 64 + pb * 32 + l32 + dx;
-          uint4 v = *reinterpret_cast<const uint4*>(X + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8));
-          if (!((tapmask[pb] >> tap) & 1u)) v = make_uint4(0, 0, 0, 0);
-          bfr[pb] = as_bf16x8(v);
-        }
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int row = dx * kConvCo + 32 * b + l32;
-          afr[b] = as_bf16x8(*reinterpret_cast<const uint4*>(Wt + row * CQ + (((2 * k + half) ^ conv_key<NCH>(row)) * 8)));
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int pb = 0; pb < 2; ++pb) acc[pb][b] = mfma32(afr[b], bfr[pb], acc[pb][b]);
+        for (int pb = 0; pb < 2; ++pb) acc[pb][b] = mfma32(afr[PAR][b], bfr[PAR][pb], acc[pb][b]);
+      if constexpr (j + 1 < NSTEP) {
+        // one MFMA, then the next step's six reads one per MFMA, then the rest
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        static_for<0, 6>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     });
   };
