@@ -52,7 +52,7 @@ ATTN_TRAFFIC = {
 # the decoder convolution, per workload, same scaling and keying
 CONV_SOURCES = ("conv3d.hip", "ust_device.h")
 CONV_TRAFFIC = {
-    "vae_conv": {"src_sha16": "047f294e4bbd3dcf", "bytes": (2 * 62823 + 32776) * 1024},
+    "vae_conv": {"src_sha16": "a69f954fab1ff211", "bytes": (2 * 62222 + 32760) * 1024},
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
@@ -484,6 +484,8 @@ def main_fused(args):
     x = xs[C]
     n_k = len(B.ust_window_plan(g, ring.abi, F0, w.n_recent)[0]) * w.T
     flops = attn_flops(w.n_q, n_k, w.head_dim, w.n_heads)
+    if args.calib_copy_mb:
+        reference_copy(args.calib_copy_mb)
 
     def step(ev=None):
         if ev is not None:
