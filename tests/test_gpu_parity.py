@@ -708,6 +708,27 @@ def test_lowrank_dense_and_bias():
     assert_close(_f64(P.from_device_bf16(y)), ref, "dense + bias")
 
 
+def test_dense_wide_product_grouped_tiles():
+    """A product that needs several rounds of the chip and whose weight does
+    not fit in one XCD's L2 (4680 x 1536 by 4608 outputs: 684 tiles, 14 MB of
+    W) runs its tiles in groups of four row blocks; the last group holds the
+    three remaining ones.  Compared in full with the fp64 oracle."""
+    w = wl.WAN_WINDOW
+    wb = np.concatenate([wl.dense_weight_bf16(w, t) for t in (wl.TAG_WQ, wl.TAG_WK, wl.TAG_WV)],
+                        axis=1)
+    xb = wl.activations(w, 1)
+    bias = wl.normal_bf16(w, (wb.shape[1],), 98)
+    M, K, N = xb.shape[0], wb.shape[0], wb.shape[1]
+    print(f"[dense grouped {M} x {K} -> {N}]", flush=True)
+    x = P.to_device_bf16(xb)
+    a = P.to_device_bf16(P.output_major(wb))
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.ust_lowrank_proj(x, a, None, P.to_device_bf16(bias), None, y, M, K, N, N)
+    torch.cuda.synchronize()
+    ref = O.lowrank_proj(_f64(xb), _f64(wb), None, _f64(bias))
+    assert_close(_f64(P.from_device_bf16(y)), ref, "dense wide product, grouped tiles")
+
+
 # ------------------------------------------------------------------ layer-chunk
 
 def test_layer_chunk_wan_window_chained():
