@@ -365,7 +365,12 @@ def main():
     del flush, csrc, cdst
     attn_tflops = flops / (attn_us * 1e-6) / 1e12
     append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
-    lowrank_flops = 2 * 2.0 * w.n_q * w.hidden * w.rank
+    # V and O projections: each (X A_r) B_r, 2 M K r + 2 M r N flop with N = K
+    lowrank_flops = 2 * 4.0 * w.n_q * w.hidden * w.rank
+    # the two projections' algorithmic bytes (X and Y, both factors) and the
+    # roofline that bounds them: min(MFMA peak, intensity x HBM peak)
+    lowrank_bytes = 2 * (2.0 * w.n_q * w.hidden * 2 + 2.0 * w.rank * w.hidden * 2)
+    lowrank_roof = min(PEAK_BF16_TFLOPS, lowrank_flops / lowrank_bytes * PEAK_HBM_GBS / 1e3)
 
     result = {
         "metric": METRIC,
@@ -428,6 +433,10 @@ def main():
                 stage["copy_same_bytes_cold_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "lowrank_v_o_TFLOPs": round(lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"])
                                                          * 1e-6) / 1e12, 1),
+            "lowrank_v_o_roofline_TFLOPs": round(lowrank_roof, 1),
+            "lowrank_v_o_frac_of_roofline": round(
+                lowrank_flops / ((stage["v_proj_us"] + stage["o_proj_us"]) * 1e-6) / 1e12
+                / lowrank_roof, 4),
         },
         "targets": {
             "attention_frac_of_bf16_peak": {"target": 0.5, "got": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
