@@ -16,6 +16,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "gemm_order.h"
 #include "ust_device.h"
 #include "ust_internal.h"
 
@@ -24,9 +25,6 @@ namespace {
 
 constexpr int kBN = 128;
 constexpr int kBK = 64;
-constexpr int kChipCUs = 256;   // compute units of the part (one round of one-per-CU tiles)
-constexpr int kGroupRows = 4;   // row blocks per group of the multi-round tile order
-constexpr int64_t kL2Bytes = int64_t(4) << 20;   // L2 of one XCD
 
 template <int MB>  // 32-row blocks of X per wave; BM = 64 * MB
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -232,27 +230,10 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   const int wm = wave % WM, wn = wave / WM;
   const int nbn = (g.N + BN - 1) / BN;
   const int nbm = (g.M + BM - 1) / BM;
-  const int ntile = nbm * nbn;
-  const int xcd = blockIdx.x & 7, q = ntile >> 3, r = ntile & 7;
-  const int tile = xcd * q + min(xcd, r) + (blockIdx.x >> 3);
-  // Within one round of the chip, or when W fits in one XCD's L2, the tiles
-  // run row-major.  When they need several rounds and W does not fit, the
-  // indices run over groups of kGroupRows row blocks, column by column, so
-  // the tiles one XCD runs at a time form a compact block (4 x 8 for 32 CUs)
-  // whose rows of X and columns of W its L2 then serves to several tiles
-  // each, instead of one row block against a run of W columns that the next
-  // row block fetches again.
-  int m0, n0;
-  if (ntile <= kChipCUs || int64_t(g.N) * g.K * 2 <= kL2Bytes) {
-    m0 = (tile / nbn) * BM;
-    n0 = (tile % nbn) * BN;
-  } else {
-    const int grp = tile / (kGroupRows * nbn), first = grp * kGroupRows;
-    const int rows = min(kGroupRows, nbm - first);
-    const int local = tile - grp * kGroupRows * nbn;
-    m0 = (first + local % rows) * BM;
-    n0 = (local / rows) * BN;
-  }
+  // XCD-aware tile order, row-major or grouped (gemm_order.h)
+  const GemmTile tl = gemm_tile(blockIdx.x, nbm, nbn, int64_t(g.N) * g.K * 2);
+  const int m0 = tl.m_blk * BM;
+  const int n0 = tl.n_blk * BN;
   const int nkt = g.K / 64;
 
   // per-lane byte offsets of this wave's loads; 8 lanes fill one 128-byte

@@ -370,6 +370,32 @@ def test_split_schedule_covers_every_tile_once(tmp_path):
     assert r.returncode == 0 and r.stdout.strip() == f"ok {len(cases)}", r.stdout
 
 
+def test_gemm_tile_order_covers_every_tile_once(tmp_path):
+    """The pipelined GEMM's tile order (gemm_order.h, shared with the kernel),
+    run on the CPU: every tile once, a contiguous run of tiles per XCD, the
+    row-major order exactly when the grid fits one round or W fits one L2,
+    and compact blocks per XCD in the grouped order."""
+    from causal_video_diffusion_amd import build
+    exe = tmp_path / "gemm_order_check"
+    src = os.path.join(ROOT, "tests", "gemm_order_check.cpp")
+    subprocess.run([build.hipcc(), "-O1", "-std=c++17", f"--offload-arch={build.ARCH}", src,
+                    "-o", str(exe)], check=True, capture_output=True)
+    cases = []
+    # the path's products (fused Q/K/V 19 x 36 with 14.2 MB of W, the projections,
+    # 720p), then grids around one round and the L2 size, and ragged last groups
+    for nbm, nbn, wb in [(19, 36, 4608 * 1536 * 2), (19, 12, 1536 * 1536 * 2),
+                         (37, 4, 512 * 1536 * 2), (19, 12, 1536 * 512 * 2),
+                         (57, 12, 1536 * 256 * 2), (25, 72, 2304 * 1536 * 2)]:
+        cases.append((nbm, nbn, wb))
+    for nbm in (1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 18, 19, 33, 64, 65):
+        for nbn in (1, 2, 3, 8, 12, 13, 36, 40, 72):
+            for wb in (1 << 20, (4 << 20), (4 << 20) + 2, 16 << 20):
+                cases.append((nbm, nbn, wb))
+    inp = "".join(f"{m} {n} {w}\n" for m, n, w in cases)
+    r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == f"ok {len(cases)}", r.stdout
+
+
 def test_status_strings(lib):
     for k, v in B.STATUS.items():
         assert lib.ust_status_str(k).decode() == v
