@@ -260,15 +260,24 @@ def main():
     # ev: None, or 5 events; all=False records only the two around the
     # attention kernel (each event costs ~2-3 µs of step time, so the timed
     # region carries only those; the per-stage split is a separate pass)
+    # the value projection stores V straight into the ring (rank a multiple
+    # of 64), and the append then moves the keys only
+    v_ring = P.v_into_ring(wv, bufs)
+
     def step(i, ev=None, all=False):
         c = steady[i % len(steady)]
         xc, qc, kc = chunks[c]
         if ev is not None and all:
             ev[0].record(stream)
-        P.lowrank_apply(wv, xc, bufs.v, bufs.t_v)
+        if v_ring:
+            B.ust_lowrank_proj_v_append(g, ring.abi, xc, wv.a, wv.b, bufs.t_v, w.hidden, w.rank,
+                                        3 * c)
+        else:
+            P.lowrank_apply(wv, xc, bufs.v, bufs.t_v)
         if ev is not None and all:
             ev[1].record(stream)
-        B.ust_kv_append(g, ring.abi, kc, bufs.v, table.cos, table.sin, w.n_tab_frames, 3 * c)
+        B.ust_kv_append(g, ring.abi, kc, None if v_ring else bufs.v, table.cos, table.sin,
+                        w.n_tab_frames, 3 * c)
         if ev is not None:
             ev[2].record(stream)
         attention(qc, 3 * c)
@@ -311,9 +320,11 @@ def main():
     names = ["v_proj_us", "rope_k_append_us", "window_attn_us", "o_proj_us"]
     stage = {n: 1000.0 * float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs]))
              for i, n in enumerate(names)}
-    # the append alone, 20 launches back to back between two events (it is
-    # idempotent: the same values into the same slots), so the per-launch
-    # time carries no event overhead
+    # the append alone (keys and values: the a3 entry point), 20 launches
+    # back to back between two events (it is idempotent: the same values into
+    # the same slots), so the per-launch time carries no event overhead; V is
+    # the chunk's value projection, the bits the step stored in the ring
+    P.lowrank_apply(wv, x, bufs.v, bufs.t_v)
     b0 = torch.cuda.Event(enable_timing=True)
     b1 = torch.cuda.Event(enable_timing=True)
     b0.record(stream)
@@ -365,6 +376,8 @@ def main():
     del flush, csrc, cdst
     attn_tflops = flops / (attn_us * 1e-6) / 1e12
     append_bytes = 4.0 * w.n_q * w.hidden * 2 + w.n_q * (w.head_dim // 2) * 8
+    # the in-step append: keys only when the V projection stores V itself
+    step_append_bytes = append_bytes - (2.0 * w.n_q * w.hidden * 2 if v_ring else 0.0)
     # V and O projections: each (X A_r) B_r, 2 M K r + 2 M r N flop with N = K
     lowrank_flops = 2 * 4.0 * w.n_q * w.hidden * w.rank
     # the two projections' algorithmic bytes (X and Y, both factors) and the
@@ -414,6 +427,10 @@ def main():
         "stages_us": {k: round(v, 2) for k, v in stage.items()},
         "stages_note": "separate untimed pass with an event between every stage "
                        "(each event adds ~2-3 us; stage times include launch gaps); "
+                       "v_proj_us: the value projection storing V straight into the ring "
+                       "(ust_lowrank_proj_v_append), then rope_k_append_us: the in-step "
+                       "append of the keys only (its GB/s over K read + written and the "
+                       "table rows); "
                        "rope_k_append_batched_us: 20 appends back to back, per launch "
                        "(no event overhead; inputs warm); rope_k_append_cold_us: 20 "
                        "(512 MiB read, append) pairs minus 20 reads alone, per append, "
@@ -422,8 +439,9 @@ def main():
                        "the same measurement for a plain device copy of the append's K and V "
                        "(28.8 MB read, 28.8 MB written), what a cold launch of that size reaches",
         "stages": {
-            "rope_k_append_GBs": round(append_bytes / (stage["rope_k_append_us"] * 1e-6) / 1e9, 1),
-            "rope_k_append_hbm_frac": round(append_bytes / (stage["rope_k_append_us"] * 1e-6)
+            "rope_k_append_GBs": round(step_append_bytes / (stage["rope_k_append_us"] * 1e-6)
+                                       / 1e9, 1),
+            "rope_k_append_hbm_frac": round(step_append_bytes / (stage["rope_k_append_us"] * 1e-6)
                                             / 1e9 / PEAK_HBM_GBS, 4),
             "rope_k_append_batched_hbm_frac": round(
                 append_bytes / (stage["rope_k_append_batched_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
@@ -960,9 +978,15 @@ def main_clip(args):
                 P.lowrank_apply(L["wk"], x, kbuf)
                 if e:
                     e[1].record(stream)
-                P.lowrank_apply(L["wv"], x, bufs.v, bufs.t_v)
-                B.ust_kv_append(g, L["ring"].abi, kbuf, bufs.v, table.cos, table.sin,
-                                w.n_tab_frames, 3 * c)
+                if P.v_into_ring(L["wv"], bufs):
+                    B.ust_lowrank_proj_v_append(g, L["ring"].abi, x, L["wv"].a, L["wv"].b,
+                                                bufs.t_v, w.hidden, w.rank, 3 * c)
+                    B.ust_kv_append(g, L["ring"].abi, kbuf, None, table.cos, table.sin,
+                                    w.n_tab_frames, 3 * c)
+                else:
+                    P.lowrank_apply(L["wv"], x, bufs.v, bufs.t_v)
+                    B.ust_kv_append(g, L["ring"].abi, kbuf, bufs.v, table.cos, table.sin,
+                                    w.n_tab_frames, 3 * c)
                 if e:
                     e[2].record(stream)
                 attention(L["ring"], c)

@@ -24,7 +24,7 @@ EXPORTS = ("ust_v_row_len", "ust_rope_table_build", "ust_kv_append",
            "ust_qkv_append", "ust_lowrank_proj", "ust_flow_step", "ust_slot_of_frame",
            "ust_window_plan", "ust_sigma_schedule", "ust_status_str", "ust_last_error",
            "ust_calib_mfma_bf16", "ust_lowrank_proj_static", "ust_conv3d_causal",
-           "ust_conv3d_causal_stream")
+           "ust_conv3d_causal_stream", "ust_lowrank_proj_v_append")
 
 
 class UstError(RuntimeError):
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         I32, P]),
         "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, P, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
+        "ust_lowrank_proj_v_append": (I32, [GP, KP, P, P, P, P, I32, I32, I32, P]),
         "ust_lowrank_proj_static": (I32, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_conv3d_causal": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
         "ust_conv3d_causal_stream": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
@@ -176,6 +177,13 @@ def ust_qkv_append(g: Geom, ring: Kv, x, w_qkv, hidden: int, cos_tab, sin_tab,
     _check(load().ust_qkv_append(ctypes.byref(g), ctypes.byref(ring), _ptr(x), _ptr(w_qkv),
                                  hidden, _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
                                  frame_start, _ptr(q_out), _stream(stream)))
+
+
+def ust_lowrank_proj_v_append(g: Geom, ring: Kv, x, a, b, t_work, hidden: int, rank: int,
+                              frame_start: int, stream=None) -> None:
+    _check(load().ust_lowrank_proj_v_append(ctypes.byref(g), ctypes.byref(ring), _ptr(x), _ptr(a),
+                                            _ptr(b), _ptr(t_work), hidden, rank, frame_start,
+                                            _stream(stream)))
 
 
 def ust_lowrank_proj(x, a, b, bias, t_work, y, M: int, K: int, r: int, N: int,

@@ -349,12 +349,13 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   }
 
   // which output of the fused projection this tile is (0 Q, 1 K, 2 V) and
-  // its head
+  // its head; a product of fewer parts starts at part e.part0
   int which = 0, h = 0;
   if constexpr (QKV) {
     const int HD = e.H * BN;
     which = n0 / HD;
     h = (n0 - which * HD) / BN;
+    which += e.part0;
   }
 
   // epilogue: bias, bf16, staged through LDS so each row leaves in 16-byte

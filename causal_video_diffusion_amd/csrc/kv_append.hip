@@ -10,6 +10,8 @@
 //           of 8 consecutive tokens per dimension into the transposed value
 //           slot [slot][h][dim][t] (the layout the attention's PV product
 //           reads without a transpose).
+// With with_v == 0 only the keys are appended (the values reach the ring
+// from the value projection's epilogue instead).
 // The work is a streaming copy with no reuse (HBM-bound).  Workgroups are
 // ordered head-fastest and XCD-aware, so the table rows of a token tile are
 // fetched from HBM once and re-read by its other heads from the same L2.
@@ -66,7 +68,7 @@ kv_append_kernel(AppendArgs a) {
     const int dc = c % CH;
     const int64_t src = ((row0 + tl) * a.H + h) * D + dc * 8;
     kw[it] = *reinterpret_cast<const uint4*>(knew + src);
-    vw[it] = *reinterpret_cast<const uint4*>(vnew + src);
+    vw[it] = a.with_v ? *reinterpret_cast<const uint4*>(vnew + src) : make_uint4(0, 0, 0, 0);
     cs[it] = *reinterpret_cast<const float4*>(ctab + tab0 + int64_t(tl) * P + dc * 4);
     sn[it] = *reinterpret_cast<const float4*>(stab + tab0 + int64_t(tl) * P + dc * 4);
   }
@@ -90,13 +92,16 @@ kv_append_kernel(AppendArgs a) {
       }
       *reinterpret_cast<uint4*>(kdst + int64_t(tl) * D + dc * 8) =
           make_uint4(kout[0], kout[1], kout[2], kout[3]);
-      uint32_t* row = vt + tl * LROW + dc * 4;
-      row[0] = vw[it].x;
-      row[1] = vw[it].y;
-      row[2] = vw[it].z;
-      row[3] = vw[it].w;
+      if (a.with_v) {
+        uint32_t* row = vt + tl * LROW + dc * 4;
+        row[0] = vw[it].x;
+        row[1] = vw[it].y;
+        row[2] = vw[it].z;
+        row[3] = vw[it].w;
+      }
     }
   }
+  if (!a.with_v) return;   // uniform over the workgroup
   __syncthreads();
 
   // transposed values: item = (dim d, group of 8 tokens)

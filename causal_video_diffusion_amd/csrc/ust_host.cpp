@@ -226,9 +226,10 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
     if (s != UST_OK) return s;
     s = check_ring_size(g, kv);
     if (s != UST_OK) return s;
-    if (!k_new || !v_new || !cos_tab || !sin_tab)
-      return fail(UST_E_NULL, "k_new, v_new or table pointer is NULL");
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_tab) || !aligned16(sin_tab))
+    if (!k_new || !cos_tab || !sin_tab)
+      return fail(UST_E_NULL, "k_new or table pointer is NULL");
+    if (!aligned16(k_new) || (v_new && !aligned16(v_new)) || !aligned16(cos_tab) ||
+        !aligned16(sin_tab))
       return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
     const int32_t T = g->grid_h * g->grid_w;
     if (T % 8 != 0)
@@ -248,6 +249,7 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
     a.D = g->head_dim;
     a.C = g->chunk_frames;
     a.frame_start = frame_start;
+    a.with_v = v_new != nullptr;
     return hip_status(ust::launch_kv_append(a, stream), "kv_append launch");
   } catch (...) {
     return fail(UST_E_HIP, "internal error");
@@ -410,6 +412,54 @@ ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
     const ust::GemmArgs ga{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qkv),
                            nullptr, nullptr, M, N, hidden};
     return hip_status(ust::launch_qkv_append(ga, e, stream), "qkv_append launch");
+  } catch (...) {
+    return fail(UST_E_HIP, "internal error");
+  }
+}
+
+ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const void* x,
+                                     const void* a, const void* b, void* t_work, int32_t hidden,
+                                     int32_t rank, int32_t frame_start, hipStream_t stream) {
+  try {
+    ust_status s = check_geom(g);
+    if (s != UST_OK) return s;
+    s = check_kv(kv);
+    if (s != UST_OK) return s;
+    s = check_ring_size(g, kv);
+    if (s != UST_OK) return s;
+    if (!x || !a || !b || !t_work) return fail(UST_E_NULL, "x, a, b or t_work is NULL");
+    if (!aligned16(x) || !aligned16(a) || !aligned16(b) || !aligned16(t_work))
+      return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
+    if (hidden <= 0 || rank <= 0)
+      return fail(UST_E_SHAPE, "hidden %d and rank %d must be positive", hidden, rank);
+    if (hidden % 8 != 0) return fail(UST_E_ALIGN, "hidden %d: must be a multiple of 8", hidden);
+    if (rank % 64 != 0)
+      return fail(UST_E_UNSUPPORTED, "rank %d: must be a multiple of 64", rank);
+    const int32_t T = g->grid_h * g->grid_w;
+    if (T % 8 != 0)
+      return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
+    const int32_t M = T * g->chunk_frames;
+    const int32_t N = g->n_heads * g->head_dim;
+    if (int64_t(M) * std::max(hidden, rank) >= (int64_t(1) << 31) ||
+        int64_t(rank) * hidden >= (int64_t(1) << 31) || int64_t(N) * rank >= (int64_t(1) << 31))
+      return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
+    ust::QkvEpilogue e{};
+    s = chunk_slots(g, kv, INT32_MAX, frame_start, e.chunk_slot);
+    if (s != UST_OK) return s;
+    e.v_cache = static_cast<uint16_t*>(kv->v);
+    e.T = T;
+    e.TV = ust_v_row_len(T);
+    e.H = g->n_heads;
+    e.D = g->head_dim;
+    e.frame_start = frame_start;
+    e.part0 = 2;   // every tile of the second product is a head of V
+    uint16_t* t = static_cast<uint16_t*>(t_work);
+    const ust::GemmArgs g1{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(a),
+                           nullptr, t, M, rank, hidden};
+    hipError_t err = ust::launch_gemm_nt(g1, stream);
+    if (err != hipSuccess) return hip_status(err, "lowrank_proj_v_append launch (X A)");
+    const ust::GemmArgs g2{t, static_cast<const uint16_t*>(b), nullptr, nullptr, M, N, rank};
+    return hip_status(ust::launch_qkv_append(g2, e, stream), "lowrank_proj_v_append launch (T B)");
   } catch (...) {
     return fail(UST_E_HIP, "internal error");
   }

@@ -29,6 +29,7 @@ struct AppendArgs {
   int32_t T, TV, H, D, C;
   int32_t frame_start;
   int32_t chunk_slot[8];     // slot of each chunk frame (C <= 8)
+  int32_t with_v;            // 0: keys only (v_new unused)
 };
 
 struct AttnArgs {
@@ -74,6 +75,7 @@ struct QkvEpilogue {
   int32_t T, TV, H, D;
   int32_t frame_start;
   int32_t chunk_slot[8];     // slot of each chunk frame
+  int32_t part0;             // output part of the product's first head-wide tiles: 0 Q, 1 K, 2 V
 };
 
 // One sampler step: x0_hat = x - sigma v, x_next = keep x0_hat + sigma_next

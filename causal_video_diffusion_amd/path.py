@@ -215,6 +215,13 @@ class LayerBuffers:
             attn_work=work)
 
 
+def v_into_ring(wv: LowRank, bufs: LayerBuffers) -> bool:
+    """Whether the value projection can store V straight into the ring: a
+    truncated-SVD projection (a second factor) whose rank is a multiple of 64,
+    with its rank-r scratch in bufs."""
+    return wv.b is not None and wv.rank % 64 == 0 and bufs.t_v is not None
+
+
 def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
                 q: torch.Tensor, k_new: torch.Tensor, wv: LowRank, wo: LowRank,
                 frame_start: int, n_recent: int, bufs: LayerBuffers,
@@ -223,10 +230,19 @@ def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
 
     x: hidden states [NQ][hidden]; q, k_new: [NQ][H*D] un-rotated (from the
     dense query/key projections).  The attention runs on the key-split
-    schedule when bufs holds its workspace."""
-    lowrank_apply(wv, x, bufs.v, bufs.t_v)
-    B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,
-                    table.n_frames, frame_start)
+    schedule when bufs holds its workspace.  A truncated-SVD value projection
+    whose rank is a multiple of 64 stores V straight into the ring
+    (ust_lowrank_proj_v_append) and the append moves the keys only; other
+    value projections go through bufs.v and the full append."""
+    if v_into_ring(wv, bufs):
+        B.ust_kv_append(g, ring.abi, k_new, None, table.cos, table.sin,
+                        table.n_frames, frame_start)
+        B.ust_lowrank_proj_v_append(g, ring.abi, x, wv.a, wv.b, bufs.t_v, wv.k_in, wv.rank,
+                                    frame_start)
+    else:
+        lowrank_apply(wv, x, bufs.v, bufs.t_v)
+        B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,
+                        table.n_frames, frame_start)
     if bufs.attn_work is not None:
         B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, table.n_frames,
                                 frame_start, n_recent, scale, bufs.o, bufs.lse,

@@ -22,6 +22,8 @@
  *                         the K/V append fused into the product's epilogue
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
+ *   ust_lowrank_proj_v_append  the value projection with the values stored
+ *                         straight into the ring's slots
  *   ust_lowrank_proj_static  the same with the intermediate in a fixed device
  *                         array, for callers that cannot allocate
  *   ust_flow_step         one step of the chunk sampler: denoised estimate and
@@ -132,9 +134,11 @@ ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double thet
  *   kv.v[slot(f)][h][:][n % T]  = v_new[n][h][:]          (bit copy)
  * The rotation is done in fp32 with the table's coefficients.  Slots of
  * other frames are not touched.
- *   k_new, v_new: bf16 [chunk_frames*T][n_heads][head_dim], read.
+ *   k_new, v_new: bf16 [chunk_frames*T][n_heads][head_dim], read.  v_new may
+ *         be NULL: then only the keys are appended (the values reach the
+ *         ring another way, e.g. ust_lowrank_proj_v_append).
  *   cos_tab, sin_tab: the table of ust_rope_table_build over n_tab_frames.
- * Errors: NULL pointers; frame_start < 0 or the chunk's frames not all
+ * Errors: NULL k_new or table; frame_start < 0 or the chunk's frames not all
  * < n_tab_frames (UST_E_RANGE); n_slots - n_sink < chunk_frames or
  * n_sink < 0 (UST_E_RANGE); misaligned pointers; T not a multiple of 8 or
  * head_dim not 64/128 (UST_E_UNSUPPORTED). */
@@ -252,6 +256,30 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b,
                             const void* bias, void* t_work, void* y,
                             int32_t M, int32_t K, int32_t r, int32_t N,
                             hipStream_t stream);
+
+/* The value projection of one chunk, V = (X A_r) B_r as ust_lowrank_proj
+ * computes it (abstract: truncated SVD of the value projection), with the
+ * values stored straight into the ring instead of a V buffer (abstract: the
+ * KV cache indexed by latent frame): for every token n of the chunk (frame
+ * f = frame_start + n / T) and head h,
+ *   kv.v[slot(f)][h][:][n % T] = bf16_rne((x[n] A_r) B_r)[h][:]
+ * with T rounded to bf16 between the two products, bit for bit the values
+ * that ust_lowrank_proj followed by ust_kv_append would store.  The keys
+ * are not touched (ust_kv_append with v_new NULL appends them).
+ *   x:      bf16 [chunk_frames*T][hidden], read.
+ *   a:      bf16 [rank][hidden], A_r output-major.  Read.
+ *   b:      bf16 [n_heads*head_dim][rank], B_r output-major.  Read.
+ *   t_work: bf16 [chunk_frames*T][rank] scratch, caller-owned (contents
+ *           unspecified after the call).
+ * Errors: NULL pointers; non-positive hidden or rank (UST_E_SHAPE); hidden
+ * not a multiple of 8 or misaligned pointers (UST_E_ALIGN); rank not a
+ * multiple of 64, T not a multiple of 8 or head_dim not 64/128
+ * (UST_E_UNSUPPORTED); frame_start < 0 or a ring that cannot hold the chunk
+ * (UST_E_RANGE); operands past 32-bit indexing (UST_E_SHAPE). */
+ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const void* x,
+                                     const void* a, const void* b, void* t_work,
+                                     int32_t hidden, int32_t rank, int32_t frame_start,
+                                     hipStream_t stream);
 
 /* Largest M * r that ust_lowrank_proj_static accepts: the bf16 elements of
  * its device scratch (8 MiB). */

@@ -708,6 +708,63 @@ def test_lowrank_dense_and_bias():
     assert_close(_f64(P.from_device_bf16(y)), ref, "dense + bias")
 
 
+@pytest.mark.parametrize("name", ["mid", "wan_window", "wan_window_d64", "wan_720p"])
+def test_lowrank_proj_v_append_equals_projection_then_append(name):
+    """The value projection stored straight into the ring, with the keys-only
+    append, leaves the ring bit for bit as ust_lowrank_proj followed by the
+    full ust_kv_append does, chunk after chunk (slots no chunk wrote and the
+    rows' padding keep the NaN fill).  On the small shape the values are also
+    compared with the fp64 oracle."""
+    w = WAN_WINDOW_D64 if name == "wan_window_d64" else wl.ALL[name]
+    g = _g(w)
+    print(f"[lowrank_proj_v_append {name}]", flush=True)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring_ref = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    a, b = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
+    p = P.LowRank.from_bits(a, b)
+    HD = w.n_heads * w.head_dim
+    t = torch.empty((w.n_q, w.rank), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((w.n_q, HD), dtype=torch.bfloat16, device="cuda")
+    n_chunks = min(w.n_chunks, 3)
+    for c in range(n_chunks):
+        xb = wl.activations(w, c)
+        x = P.to_device_bf16(xb)
+        k = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_K, c).reshape(w.n_q, -1))
+        P.lowrank_apply(p, x, v, t)
+        B.ust_kv_append(g, ring_ref.abi, k, v, table.cos, table.sin, w.n_tab_frames, 3 * c)
+        B.ust_kv_append(g, ring.abi, k, None, table.cos, table.sin, w.n_tab_frames, 3 * c)
+        B.ust_lowrank_proj_v_append(g, ring.abi, x, p.a, p.b, t, w.hidden, w.rank, 3 * c)
+    torch.cuda.synchronize()
+    assert torch.equal(ring.k.view(torch.int16), ring_ref.k.view(torch.int16))
+    assert torch.equal(ring.v.view(torch.int16), ring_ref.v.view(torch.int16))
+    if name == "mid":
+        c = n_chunks - 1
+        ref = O.lowrank_proj(_f64(wl.activations(w, c)), _f64(a), _f64(b))
+        ref = ref.reshape(3, w.T, w.n_heads, w.head_dim)
+        gv = ring.host_v_natural()          # [slot][h][t][d]
+        got = np.stack([gv[O.slot_of_frame(3 * c + i, w.n_slots, w.n_sink)].transpose(1, 0, 2)
+                        for i in range(3)])
+        assert_close(_f64(got), ref, "values in the ring")
+
+
+def test_keys_only_append_leaves_values():
+    """ust_kv_append with v_new NULL writes the keys of the chunk's slots and
+    no value."""
+    w = wl.MID
+    g = _g(w)
+    table = P.RopeTable(g, w.n_tab_frames, w.theta)
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    ring_full = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    k = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_K, 1).reshape(w.n_q, -1))
+    v = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_V, 1).reshape(w.n_q, -1))
+    B.ust_kv_append(g, ring.abi, k, None, table.cos, table.sin, w.n_tab_frames, 3)
+    B.ust_kv_append(g, ring_full.abi, k, v, table.cos, table.sin, w.n_tab_frames, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(ring.k.view(torch.int16), ring_full.k.view(torch.int16))
+    assert np.all(P.from_device_bf16(ring.v) == NAN_BITS)
+
+
 def test_dense_wide_product_grouped_tiles():
     """A product that needs several rounds of the chip and whose weight does
     not fit in one XCD's L2 (4680 x 1536 by 4608 outputs: 684 tiles, 14 MB of

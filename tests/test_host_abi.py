@@ -40,7 +40,7 @@ def _header_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = _header_symbols()
-    assert len(syms) == 18
+    assert len(syms) == 19
     assert sorted(B.EXPORTS) == syms
     for s in syms:
         assert hasattr(lib, s), s
@@ -282,6 +282,31 @@ def test_qkv_append_rejects_bad_arguments(lib):
     small = B.Kv(fake, fake, 4, 3)
     assert _raw(lib, "ust_qkv_append", gp, ctypes.byref(small), fake, fake, 1536, fake, fake,
                 21, 6, fake, None)[0] == "UST_E_RANGE"
+
+
+def test_lowrank_proj_v_append_rejects_bad_arguments(lib):
+    """The value projection into the ring validates the geometry, the ring
+    and its operands before any launch; misaligned v_new is still rejected
+    by ust_kv_append (NULL v_new is the keys-only form)."""
+    w = wl.WAN_WINDOW
+    g = _geom(w)
+    fake = 0x10000
+    ring = B.Kv(fake, fake, 21, 3)
+    gp, rp = ctypes.byref(g), ctypes.byref(ring)
+    call = lambda x, t, hidden, rank, f0, rr=rp: _raw(lib, "ust_lowrank_proj_v_append", gp, rr, x,
+                                                     fake, fake, t, hidden, rank, f0, None)
+    assert call(None, fake, 1536, 512, 0)[0] == "UST_E_NULL"
+    assert call(fake, None, 1536, 512, 0)[0] == "UST_E_NULL"
+    assert call(fake + 8, fake, 1536, 512, 0)[0] == "UST_E_ALIGN"
+    assert call(fake, fake, 0, 512, 0)[0] == "UST_E_SHAPE"
+    assert call(fake, fake, 1536, -64, 0)[0] == "UST_E_SHAPE"
+    assert call(fake, fake, 1540, 512, 0)[0] == "UST_E_ALIGN"          # hidden % 8
+    assert call(fake, fake, 1536, 520, 0)[0] == "UST_E_UNSUPPORTED"    # rank % 64
+    assert call(fake, fake, 1536, 512, -3)[0] == "UST_E_RANGE"
+    small = B.Kv(fake, fake, 4, 3)
+    assert call(fake, fake, 1536, 512, 6, ctypes.byref(small))[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake + 2, fake, fake, 21, 0,
+                None)[0] == "UST_E_ALIGN"
 
 
 def test_flow_step_rejects_bad_arguments(lib):
