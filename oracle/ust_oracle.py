@@ -14,7 +14,8 @@ Layouts used here (the oracle's own, chosen for readability):
   chunk tensors q, k_new, v_new : [chunk_frames*T][H][D]; token n is frame
       frame_start + n // T at (y, x) = divmod(n % T, grid_w)
   cache k, v                    : [n_slots][H][T][D]
-  RoPE table cos, sin           : [n_frames][grid_h][grid_w][P], P = D/2
+  RoPE table cos, sin           : [n_frames][grid_h][grid_w][P], P = D/2;
+      row i holds frame first_frame + i (0 unless a call says otherwise)
 
 Readings of points the paper leaves open are marked READING.
 """
@@ -65,12 +66,15 @@ def rope_frequencies(pairs: Sequence[int], theta: float) -> np.ndarray:
 
 
 def rope_table(n_frames: int, grid_h: int, grid_w: int, pairs: Sequence[int],
-               theta: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Cached coefficients: cos and sin of every (frame, row, col, pair) angle."""
+               theta: float, first_frame: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Cached coefficients: cos and sin of every (frame, row, col, pair) angle,
+    for the frames first_frame .. first_frame + n_frames - 1 (row i holds
+    frame first_frame + i; the position on the temporal axis is the absolute
+    frame)."""
     P = sum(pairs)
     freq = rope_frequencies(pairs, theta)
     axis = np.array([pair_axis(p, pairs)[0] for p in range(P)])
-    f = np.arange(n_frames, dtype=np.float64)[:, None, None, None]
+    f = (first_frame + np.arange(n_frames, dtype=np.float64))[:, None, None, None]
     y = np.arange(grid_h, dtype=np.float64)[None, :, None, None]
     x = np.arange(grid_w, dtype=np.float64)[None, None, :, None]
     pos = np.where(axis == 0, f, np.where(axis == 1, y, x))   # broadcast to 4-D
@@ -161,9 +165,10 @@ class KVCache:
 def kv_append(cache: KVCache, k_new: np.ndarray, v_new: np.ndarray,
               cos_tab: np.ndarray, sin_tab: np.ndarray, frame_start: int,
               chunk_frames: int, grid_h: int, grid_w: int, n_slots: int,
-              n_sink: int) -> None:
+              n_sink: int, tab_first: int = 0) -> None:
     """Write one chunk's keys (rotated at their own position) and values into
-    the slots of its frames; every other slot is left as it was."""
+    the slots of its frames; every other slot is left as it was.  Row f -
+    tab_first of the table holds frame f."""
     T = grid_h * grid_w
     k_new = np.asarray(k_new, dtype=np.float64)
     v_new = np.asarray(v_new, dtype=np.float64)
@@ -171,8 +176,8 @@ def kv_append(cache: KVCache, k_new: np.ndarray, v_new: np.ndarray,
         f = frame_start + i
         s = slot_of_frame(f, n_slots, n_sink)
         rows = slice(i * T, (i + 1) * T)
-        c = cos_tab[f].reshape(T, -1)[:, None, :]
-        sn = sin_tab[f].reshape(T, -1)[:, None, :]
+        c = cos_tab[f - tab_first].reshape(T, -1)[:, None, :]
+        sn = sin_tab[f - tab_first].reshape(T, -1)[:, None, :]
         kr = rope_apply(k_new[rows], c, sn)            # [T][H][D]
         cache.k[s] = kr.transpose(1, 0, 2)
         cache.v[s] = v_new[rows].transpose(1, 0, 2)
@@ -188,11 +193,12 @@ def window_attn(cache: KVCache, q: np.ndarray, cos_tab: np.ndarray,
                 sin_tab: np.ndarray, frame_start: int, chunk_frames: int,
                 grid_h: int, grid_w: int, n_slots: int, n_sink: int,
                 n_recent: int, scale: Optional[float] = None,
-                rows: Optional[np.ndarray] = None, block: int = 1024
-                ) -> Tuple[np.ndarray, np.ndarray]:
+                rows: Optional[np.ndarray] = None, block: int = 1024,
+                tab_first: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of the chunk's queries over the window keys.
 
-    q: [chunk_frames*T][H][D] un-rotated.  Returns O [n][H][D] for the query
+    q: [chunk_frames*T][H][D] un-rotated; row f - tab_first of the table
+    holds frame f.  Returns O [n][H][D] for the query
     rows asked for (all by default) and the natural-log sum of exponentials of
     the scaled scores, lse [H][n].  The softmax is materialised per block of
     query rows (no online rescaling)."""
@@ -207,8 +213,8 @@ def window_attn(cache: KVCache, q: np.ndarray, cos_tab: np.ndarray,
     frames, slots = window_slots(frame_start, chunk_frames, n_sink, n_recent,
                                  n_slots)
     f, y, x = chunk_positions(frame_start, chunk_frames, grid_h, grid_w)
-    c = cos_tab[f[rows], y[rows], x[rows]][:, None, :]
-    s = sin_tab[f[rows], y[rows], x[rows]][:, None, :]
+    c = cos_tab[f[rows] - tab_first, y[rows], x[rows]][:, None, :]
+    s = sin_tab[f[rows] - tab_first, y[rows], x[rows]][:, None, :]
     qr = rope_apply(q[rows], c, s)                     # [n][H][D]
     Kw = cache.k[slots]                                # [nf][H][T][D]
     Vw = cache.v[slots]

@@ -134,6 +134,67 @@ def test_rope_matches_complex_brute_force():
                 assert np.max(np.abs(a - np.array(b))) < 1e-13
 
 
+def test_rope_table_from_a_later_frame():
+    """A table that starts at frame F holds, bit for bit, the rows the table
+    from frame 0 holds for those frames.  Far past any clip (F ~ 10^6) the
+    first temporal pair (frequency theta^0 = 1) turns by the frame index
+    itself, and every rotation agrees with the complex brute force."""
+    w = wl.TINY
+    full_c, full_s = O.rope_table(12, w.grid_h, w.grid_w, w.pairs, w.theta)
+    c, s = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=7)
+    assert np.array_equal(c, full_c[7:10]) and np.array_equal(s, full_s[7:10])
+    F = 1_000_003
+    c, s = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=F)
+    for i in range(3):
+        assert abs(c[i, 1, 2, 0] - math.cos(F + i)) < 1e-15
+        assert abs(s[i, 1, 2, 0] - math.sin(F + i)) < 1e-15
+    rs = np.random.default_rng(61)
+    for _ in range(40):
+        i, y, x = rs.integers(0, 3), rs.integers(0, w.grid_h), rs.integers(0, w.grid_w)
+        u = rs.standard_normal(w.head_dim)
+        a = O.rope_apply(u, c[i, y, x], s[i, y, x])
+        b = brute.rope_rotate(list(u), F + int(i), int(y), int(x), w.pairs, w.theta)
+        assert np.max(np.abs(a - np.array(b))) < 1e-12
+
+
+def test_stream_shifted_far_keeps_attention():
+    """Scores under RoPE depend only on position offsets.  With no sink
+    frames, three chunks appended 10^6 frames into a stream, each with a
+    table that starts at its own first frame, give the last chunk the
+    attention output of the same three chunks at the start of the stream.
+    A table row taken for the wrong frame (an offset dropped in the append
+    or in the attention) breaks the equality or the indexing."""
+    w = wl.TINY
+    n_slots, n_sink, n_recent = 9, 0, 6
+    rs = np.random.default_rng(62)
+    n = 3 * w.T
+    ks = [rs.standard_normal((n, w.n_heads, w.head_dim)) for _ in range(3)]
+    vs = [rs.standard_normal((n, w.n_heads, w.head_dim)) for _ in range(3)]
+    q = rs.standard_normal((n, w.n_heads, w.head_dim))
+    outs = []
+    for base in (0, 999_999):
+        cache = O.KVCache(n_slots, w.n_heads, w.T, w.head_dim)
+        for c in range(3):
+            f0 = base + 3 * c
+            cos, sin = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=f0)
+            O.kv_append(cache, ks[c], vs[c], cos, sin, f0, 3, w.grid_h, w.grid_w, n_slots,
+                        n_sink, tab_first=f0)
+        outs.append(O.window_attn(cache, q, cos, sin, base + 6, 3, w.grid_h, w.grid_w,
+                                  n_slots, n_sink, n_recent, tab_first=base + 6))
+    (o0, l0), (o1, l1) = outs
+    assert np.max(np.abs(o0 - o1)) < 1e-8 and np.max(np.abs(l0 - l1)) < 1e-8
+    # and the shift is not a no-op: the far stream's keys differ from the near ones
+    cache_far = O.KVCache(n_slots, w.n_heads, w.T, w.head_dim)
+    cos, sin = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=999_999)
+    O.kv_append(cache_far, ks[0], vs[0], cos, sin, 999_999, 3, w.grid_h, w.grid_w, n_slots,
+                n_sink, tab_first=999_999)
+    cache_near = O.KVCache(n_slots, w.n_heads, w.T, w.head_dim)
+    cos, sin = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta)
+    O.kv_append(cache_near, ks[0], vs[0], cos, sin, 0, 3, w.grid_h, w.grid_w, n_slots, n_sink)
+    s_far = O.slot_of_frame(999_999, n_slots, n_sink)
+    assert np.max(np.abs(cache_far.k[s_far] - cache_near.k[0])) > 1e-2
+
+
 # ---------------------------------------------------------------- slots and window
 
 @pytest.mark.parametrize("n_slots,n_sink", [(9, 1), (7, 1), (21, 3), (15, 3),
