@@ -1,7 +1,10 @@
 """ctypes binding of libust.so: same names as the C ABI, argument marshalling only.
 
 Tensors are torch tensors on the GPU; the binding passes their data pointers
-and torch's current HIP stream.  Every step of the path runs in the library's
+and torch's current HIP stream.  The C argument that names a RoPE table's
+first frame (first_frame of ust_rope_table_build, tab_first_frame of its
+consumers) is a keyword argument here, last, defaulting to 0: a table from
+frame 0.  Every step of the path runs in the library's
 kernels.  If libust.so has not been built, loading raises: there is no CPU
 fallback.
 """
@@ -64,13 +67,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     IP = ctypes.POINTER(ctypes.c_int32)
     sig = {
         "ust_v_row_len": (I32, [I32]),
-        "ust_rope_table_build": (I32, [GP, I32, F64, P, P, P]),
-        "ust_kv_append": (I32, [GP, KP, P, P, P, P, I32, I32, P]),
-        "ust_window_attn": (I32, [GP, KP, P, P, P, I32, I32, I32, F32, P, P, P]),
+        "ust_rope_table_build": (I32, [GP, I32, I32, F64, P, P, P]),
+        "ust_kv_append": (I32, [GP, KP, P, P, P, P, I32, I32, I32, P]),
+        "ust_window_attn": (I32, [GP, KP, P, P, P, I32, I32, I32, I32, F32, P, P, P]),
         "ust_window_attn_work_bytes": (SZ, [GP, I32]),
-        "ust_window_attn_split": (I32, [GP, KP, P, P, P, I32, I32, I32, F32, P, P, P, SZ,
+        "ust_window_attn_split": (I32, [GP, KP, P, P, P, I32, I32, I32, I32, F32, P, P, P, SZ,
                                         I32, P]),
-        "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, P, P]),
+        "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, I32, P, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_lowrank_proj_v_append": (I32, [GP, KP, P, P, P, P, I32, I32, I32, P]),
         "ust_lowrank_proj_static": (I32, [P, P, P, P, P, I32, I32, I32, I32, P]),
@@ -134,23 +137,24 @@ def ust_v_row_len(T: int) -> int:
 
 
 def ust_rope_table_build(g: Geom, n_frames: int, theta: float, cos_out, sin_out,
-                         stream=None) -> None:
-    _check(load().ust_rope_table_build(ctypes.byref(g), n_frames, theta,
+                         stream=None, first_frame: int = 0) -> None:
+    _check(load().ust_rope_table_build(ctypes.byref(g), first_frame, n_frames, theta,
                                        _ptr(cos_out), _ptr(sin_out), _stream(stream)))
 
 
 def ust_kv_append(g: Geom, ring: Kv, k_new, v_new, cos_tab, sin_tab,
-                  n_tab_frames: int, frame_start: int, stream=None) -> None:
+                  n_tab_frames: int, frame_start: int, stream=None,
+                  tab_first_frame: int = 0) -> None:
     _check(load().ust_kv_append(ctypes.byref(g), ctypes.byref(ring), _ptr(k_new),
-                                _ptr(v_new), _ptr(cos_tab), _ptr(sin_tab),
+                                _ptr(v_new), _ptr(cos_tab), _ptr(sin_tab), tab_first_frame,
                                 n_tab_frames, frame_start, _stream(stream)))
 
 
 def ust_window_attn(g: Geom, ring: Kv, q, cos_tab, sin_tab, n_tab_frames: int,
                     frame_start: int, n_recent: int, scale: float, out,
-                    lse=None, stream=None) -> None:
+                    lse=None, stream=None, tab_first_frame: int = 0) -> None:
     _check(load().ust_window_attn(ctypes.byref(g), ctypes.byref(ring), _ptr(q),
-                                  _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
+                                  _ptr(cos_tab), _ptr(sin_tab), tab_first_frame, n_tab_frames,
                                   frame_start, n_recent, scale, _ptr(out),
                                   _ptr(lse), _stream(stream)))
 
@@ -162,21 +166,23 @@ def ust_window_attn_work_bytes(g: Geom, n_workgroups: int = 0) -> int:
 def ust_window_attn_split(g: Geom, ring: Kv, q, cos_tab, sin_tab, n_tab_frames: int,
                           frame_start: int, n_recent: int, scale: float, out,
                           lse=None, work=None, n_workgroups: int = 0,
-                          stream=None) -> None:
+                          stream=None, tab_first_frame: int = 0) -> None:
     """work: a device tensor of at least ust_window_attn_work_bytes bytes."""
     nbytes = 0 if work is None else work.numel() * work.element_size()
     _check(load().ust_window_attn_split(ctypes.byref(g), ctypes.byref(ring), _ptr(q),
-                                        _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
+                                        _ptr(cos_tab), _ptr(sin_tab), tab_first_frame,
+                                        n_tab_frames,
                                         frame_start, n_recent, scale, _ptr(out),
                                         _ptr(lse), _ptr(work), nbytes, n_workgroups,
                                         _stream(stream)))
 
 
 def ust_qkv_append(g: Geom, ring: Kv, x, w_qkv, hidden: int, cos_tab, sin_tab,
-                   n_tab_frames: int, frame_start: int, q_out, stream=None) -> None:
+                   n_tab_frames: int, frame_start: int, q_out, stream=None,
+                   tab_first_frame: int = 0) -> None:
     _check(load().ust_qkv_append(ctypes.byref(g), ctypes.byref(ring), _ptr(x), _ptr(w_qkv),
-                                 hidden, _ptr(cos_tab), _ptr(sin_tab), n_tab_frames,
-                                 frame_start, _ptr(q_out), _stream(stream)))
+                                 hidden, _ptr(cos_tab), _ptr(sin_tab), tab_first_frame,
+                                 n_tab_frames, frame_start, _ptr(q_out), _stream(stream)))
 
 
 def ust_lowrank_proj_v_append(g: Geom, ring: Kv, x, a, b, t_work, hidden: int, rank: int,

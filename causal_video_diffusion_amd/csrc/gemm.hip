@@ -440,7 +440,7 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
       if (m < g.M) {
         const float4 xa = *reinterpret_cast<const float4*>(ldsf + rrow * ESF + c * 8);
         const float4 xb = *reinterpret_cast<const float4*>(ldsf + rrow * ESF + c * 8 + 4);
-        const int64_t trow = (int64_t(e.frame_start) * e.T + m) * (BN / 2) + c * 4;
+        const int64_t trow = (int64_t(e.tab_frame) * e.T + m) * (BN / 2) + c * 4;
         const float4 cs = *reinterpret_cast<const float4*>(e.cos_tab + trow);
         const float4 sn = *reinterpret_cast<const float4*>(e.sin_tab + trow);
         const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};

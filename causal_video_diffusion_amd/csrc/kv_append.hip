@@ -51,7 +51,7 @@ kv_append_kernel(AppendArgs a) {
   const int nt = min(kTok, a.T - t0);            // tokens here, a multiple of 8
   const int slot = a.chunk_slot[fi];
   const int64_t row0 = int64_t(fi) * a.T + t0;   // chunk token index of t0
-  const int64_t tab0 = (int64_t(a.frame_start) * a.T + row0) * P;
+  const int64_t tab0 = (int64_t(a.tab_frame) * a.T + row0) * P;
   const uint16_t* __restrict__ knew = a.k_new;
   const uint16_t* __restrict__ vnew = a.v_new;
   const float* __restrict__ ctab = a.cos_tab;

@@ -1,6 +1,8 @@
 // Cached 3-D RoPE coefficients (UnStep, abstract: RoPE is applied from
 // precomputed coefficients).  One thread per (frame, row, col, pair); angles in fp64,
-// stored as fp32.  Runs once per geometry, so it is written for clarity.
+// stored as fp32.  Row f of the table is the absolute frame first_frame + f.
+// Runs once per geometry (or once per chunk for a table of the chunk's
+// frames), so it is written for clarity.
 
 #include "ust_internal.h"
 
@@ -20,7 +22,7 @@ rope_table_kernel(RopeTableArgs a) {
   const int f = int(tok / (int64_t(a.grid_w) * a.grid_h));
   int pos, j, n;
   if (p < a.pairs_t) {
-    pos = f; j = p; n = a.pairs_t;
+    pos = a.first_frame + f; j = p; n = a.pairs_t;
   } else if (p < a.pairs_t + a.pairs_h) {
     pos = y; j = p - a.pairs_t; n = a.pairs_h;
   } else {

@@ -84,13 +84,16 @@ ust_status check_ring_size(const ust_geom* g, const ust_kv* kv) {
 }
 
 // Slots of the chunk's own frames; they must be distinct and the frames must
-// lie in the table.
-ust_status chunk_slots(const ust_geom* g, const ust_kv* kv, int32_t n_tab_frames,
+// lie in the table, which holds frames tab_first .. tab_first + n_tab - 1.
+ust_status chunk_slots(const ust_geom* g, const ust_kv* kv, int32_t tab_first, int32_t n_tab,
                        int32_t frame_start, int32_t* slots) {
   if (frame_start < 0) return fail(UST_E_RANGE, "frame_start %d < 0", frame_start);
-  if (int64_t(frame_start) + g->chunk_frames > n_tab_frames)
-    return fail(UST_E_RANGE, "frames %d..%d outside the RoPE table of %d frames", frame_start,
-                frame_start + g->chunk_frames - 1, n_tab_frames);
+  if (tab_first < 0) return fail(UST_E_RANGE, "tab_first_frame %d < 0", tab_first);
+  if (frame_start < tab_first ||
+      int64_t(frame_start) + g->chunk_frames > int64_t(tab_first) + n_tab)
+    return fail(UST_E_RANGE, "frames %d..%lld outside the RoPE table of frames %d..%lld",
+                frame_start, (long long)frame_start + g->chunk_frames - 1, tab_first,
+                (long long)tab_first + n_tab - 1);
   for (int i = 0; i < g->chunk_frames; ++i) {
     slots[i] = slot_of(frame_start + i, kv->n_slots, kv->n_sink);
     for (int j = 0; j < i; ++j)
@@ -196,8 +199,9 @@ ust_status ust_window_plan(const ust_geom* g, const ust_kv* kv, int32_t frame_st
   }
 }
 
-ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double theta,
-                                float* cos_out, float* sin_out, hipStream_t stream) {
+ust_status ust_rope_table_build(const ust_geom* g, int32_t first_frame, int32_t n_frames,
+                                double theta, float* cos_out, float* sin_out,
+                                hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
@@ -206,9 +210,12 @@ ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double thet
       return fail(UST_E_ALIGN, "table pointers must be 16-byte aligned");
     if (n_frames <= 0) return fail(UST_E_SHAPE, "n_frames %d <= 0", n_frames);
     if (!(theta > 0.0) || !std::isfinite(theta)) return fail(UST_E_RANGE, "theta must be > 0");
+    if (first_frame < 0) return fail(UST_E_RANGE, "first_frame %d < 0", first_frame);
+    if (int64_t(first_frame) + n_frames - 1 > INT32_MAX)
+      return fail(UST_E_RANGE, "frames %d + %d pass INT32_MAX", first_frame, n_frames);
     if (int64_t(n_frames) * g->grid_h * g->grid_w * (g->head_dim / 2) >= (int64_t(1) << 31))
       return fail(UST_E_SHAPE, "table too large for 32-bit indexing");
-    ust::RopeTableArgs a{cos_out, sin_out, n_frames, g->grid_h, g->grid_w,
+    ust::RopeTableArgs a{cos_out, sin_out, first_frame, n_frames, g->grid_h, g->grid_w,
                          g->pairs_t, g->pairs_h, g->pairs_w, theta};
     return hip_status(ust::launch_rope_table(a, stream), "rope_table launch");
   } catch (...) {
@@ -218,7 +225,8 @@ ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double thet
 
 ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
                          const void* v_new, const float* cos_tab, const float* sin_tab,
-                         int32_t n_tab_frames, int32_t frame_start, hipStream_t stream) {
+                         int32_t tab_first_frame, int32_t n_tab_frames, int32_t frame_start,
+                         hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
@@ -235,7 +243,7 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
     if (T % 8 != 0)
       return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
     ust::AppendArgs a{};
-    s = chunk_slots(g, kv, n_tab_frames, frame_start, a.chunk_slot);
+    s = chunk_slots(g, kv, tab_first_frame, n_tab_frames, frame_start, a.chunk_slot);
     if (s != UST_OK) return s;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
@@ -248,7 +256,7 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv, const void* k_new,
     a.H = g->n_heads;
     a.D = g->head_dim;
     a.C = g->chunk_frames;
-    a.frame_start = frame_start;
+    a.tab_frame = frame_start - tab_first_frame;
     a.with_v = v_new != nullptr;
     return hip_status(ust::launch_kv_append(a, stream), "kv_append launch");
   } catch (...) {
@@ -272,9 +280,10 @@ constexpr int32_t kMaxAttnWorkgroups = 1 << 16;
 
 // ust_window_attn (work == nullptr) and ust_window_attn_split
 ust_status window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
-                       const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
-                       int32_t frame_start, int32_t n_recent, float scale, void* out,
-                       float* lse_opt, bool split, void* work, size_t work_bytes,
+                       const float* cos_tab, const float* sin_tab, int32_t tab_first_frame,
+                       int32_t n_tab_frames, int32_t frame_start, int32_t n_recent,
+                       float scale, void* out, float* lse_opt, bool split, void* work,
+                       size_t work_bytes,
                        int32_t n_workgroups, hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
@@ -293,7 +302,7 @@ ust_status window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
       return fail(UST_E_UNSUPPORTED, "tokens per frame %d: must be a multiple of 8", T);
     if (!std::isfinite(scale) || scale < 0.f) return fail(UST_E_RANGE, "scale must be >= 0");
     int32_t cslots[8];
-    s = chunk_slots(g, kv, n_tab_frames, frame_start, cslots);
+    s = chunk_slots(g, kv, tab_first_frame, n_tab_frames, frame_start, cslots);
     if (s != UST_OK) return s;
     ust::AttnArgs a{};
     int32_t frames[UST_MAX_WINDOW_FRAMES];
@@ -315,7 +324,7 @@ ust_status window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
     a.H = g->n_heads;
     a.D = g->head_dim;
     a.NQ = T * g->chunk_frames;
-    a.frame_start = frame_start;
+    a.tab_frame = frame_start - tab_first_frame;
     a.n_frames = n;
     a.qscale = sc * 1.4426950408889634f;  // log2(e): softmax runs in base 2
     if (split) {
@@ -343,11 +352,12 @@ ust_status window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
 extern "C" {
 
 ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
-                           const float* cos_tab, const float* sin_tab, int32_t n_tab_frames,
-                           int32_t frame_start, int32_t n_recent, float scale, void* out,
-                           float* lse_opt, hipStream_t stream) {
-  return window_attn(g, kv, q, cos_tab, sin_tab, n_tab_frames, frame_start, n_recent, scale,
-                     out, lse_opt, false, nullptr, 0, 0, stream);
+                           const float* cos_tab, const float* sin_tab,
+                           int32_t tab_first_frame, int32_t n_tab_frames, int32_t frame_start,
+                           int32_t n_recent, float scale, void* out, float* lse_opt,
+                           hipStream_t stream) {
+  return window_attn(g, kv, q, cos_tab, sin_tab, tab_first_frame, n_tab_frames, frame_start,
+                     n_recent, scale, out, lse_opt, false, nullptr, 0, 0, stream);
 }
 
 size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups) {
@@ -363,17 +373,20 @@ size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups) {
 
 ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void* q,
                                  const float* cos_tab, const float* sin_tab,
-                                 int32_t n_tab_frames, int32_t frame_start, int32_t n_recent,
-                                 float scale, void* out, float* lse_opt, void* work,
-                                 size_t work_bytes, int32_t n_workgroups, hipStream_t stream) {
-  return window_attn(g, kv, q, cos_tab, sin_tab, n_tab_frames, frame_start, n_recent, scale,
-                     out, lse_opt, true, work, work_bytes, n_workgroups, stream);
+                                 int32_t tab_first_frame, int32_t n_tab_frames,
+                                 int32_t frame_start, int32_t n_recent, float scale, void* out,
+                                 float* lse_opt, void* work, size_t work_bytes,
+                                 int32_t n_workgroups, hipStream_t stream) {
+  return window_attn(g, kv, q, cos_tab, sin_tab, tab_first_frame, n_tab_frames, frame_start,
+                     n_recent, scale, out, lse_opt, true, work, work_bytes, n_workgroups,
+                     stream);
 }
 
 ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
                           const void* w_qkv, int32_t hidden, const float* cos_tab,
-                          const float* sin_tab, int32_t n_tab_frames, int32_t frame_start,
-                          void* q_out, hipStream_t stream) {
+                          const float* sin_tab, int32_t tab_first_frame,
+                          int32_t n_tab_frames, int32_t frame_start, void* q_out,
+                          hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
@@ -397,7 +410,7 @@ ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
     if (int64_t(M) * hidden >= (int64_t(1) << 31) || int64_t(N) * hidden >= (int64_t(1) << 31))
       return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
     ust::QkvEpilogue e{};
-    s = chunk_slots(g, kv, n_tab_frames, frame_start, e.chunk_slot);
+    s = chunk_slots(g, kv, tab_first_frame, n_tab_frames, frame_start, e.chunk_slot);
     if (s != UST_OK) return s;
     e.q_out = static_cast<uint16_t*>(q_out);
     e.k_cache = static_cast<uint16_t*>(kv->k);
@@ -408,7 +421,7 @@ ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
     e.TV = ust_v_row_len(T);
     e.H = g->n_heads;
     e.D = g->head_dim;
-    e.frame_start = frame_start;
+    e.tab_frame = frame_start - tab_first_frame;
     const ust::GemmArgs ga{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qkv),
                            nullptr, nullptr, M, N, hidden};
     return hip_status(ust::launch_qkv_append(ga, e, stream), "qkv_append launch");
@@ -444,14 +457,15 @@ ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const 
         int64_t(rank) * hidden >= (int64_t(1) << 31) || int64_t(N) * rank >= (int64_t(1) << 31))
       return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
     ust::QkvEpilogue e{};
-    s = chunk_slots(g, kv, INT32_MAX, frame_start, e.chunk_slot);
+    // no table: the values are not rotated
+    s = chunk_slots(g, kv, 0, INT32_MAX, frame_start, e.chunk_slot);
     if (s != UST_OK) return s;
     e.v_cache = static_cast<uint16_t*>(kv->v);
     e.T = T;
     e.TV = ust_v_row_len(T);
     e.H = g->n_heads;
     e.D = g->head_dim;
-    e.frame_start = frame_start;
+    e.tab_frame = 0;
     e.part0 = 2;   // every tile of the second product is a head of V
     uint16_t* t = static_cast<uint16_t*>(t_work);
     const ust::GemmArgs g1{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(a),

@@ -14,6 +14,7 @@ namespace ust {
 struct RopeTableArgs {
   float* cos_out;
   float* sin_out;
+  int32_t first_frame;       // absolute frame of row 0
   int32_t n_frames, grid_h, grid_w;
   int32_t pairs_t, pairs_h, pairs_w;
   double theta;
@@ -22,26 +23,26 @@ struct RopeTableArgs {
 struct AppendArgs {
   const uint16_t* k_new;     // [C*T][H][D]
   const uint16_t* v_new;     // [C*T][H][D]
-  const float* cos_tab;      // [F][T][P]
+  const float* cos_tab;      // [F][T][P], row f = frame tab_first + f
   const float* sin_tab;
   uint16_t* k_cache;         // [slots][H][T][D]
   uint16_t* v_cache;         // [slots][H][D][TV]
   int32_t T, TV, H, D, C;
-  int32_t frame_start;
+  int32_t tab_frame;         // table row frame of the chunk's first token
   int32_t chunk_slot[8];     // slot of each chunk frame (C <= 8)
   int32_t with_v;            // 0: keys only (v_new unused)
 };
 
 struct AttnArgs {
   const uint16_t* q;         // [NQ][H][D] un-rotated
-  const float* cos_tab;      // [F][T][P]
+  const float* cos_tab;      // [F][T][P], row f = frame tab_first + f
   const float* sin_tab;
   const uint16_t* k_cache;   // [slots][H][T][D]
   const uint16_t* v_cache;   // [slots][H][D][TV]
   uint16_t* out;             // [NQ][H][D]
   float* lse;                // [H][NQ] or nullptr
   int32_t T, TV, H, D, NQ;
-  int32_t frame_start;       // absolute frame of query token 0
+  int32_t tab_frame;         // table row frame of query token 0
   int32_t n_frames;          // frames in the window
   float qscale;              // scale * log2(e), folded into the rotated query
   // Schedule (attn_schedule.h).  work_o == nullptr: one workgroup per
@@ -70,10 +71,10 @@ struct QkvEpilogue {
   uint16_t* q_out;           // [M][H][D]
   uint16_t* k_cache;         // [slots][H][T][D]
   uint16_t* v_cache;         // [slots][H][D][TV]
-  const float* cos_tab;      // [F][T][P]
+  const float* cos_tab;      // [F][T][P], row f = frame tab_first + f
   const float* sin_tab;
   int32_t T, TV, H, D;
-  int32_t frame_start;
+  int32_t tab_frame;         // table row frame of the chunk's first token
   int32_t chunk_slot[8];     // slot of each chunk frame
   int32_t part0;             // output part of the product's first head-wide tiles: 0 Q, 1 K, 2 V
 };

@@ -249,7 +249,7 @@ window_attn_kernel(AttnArgs a) {
     bf16x8 qf[KS];
     {
       const uint16_t* qp = a.q + (int64_t(qn) * a.H + h) * D;
-      const int64_t trow = (int64_t(a.frame_start) * T + qn) * (D / 2);
+      const int64_t trow = (int64_t(a.tab_frame) * T + qn) * (D / 2);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int d0 = 16 * s + 8 * half;

@@ -73,15 +73,28 @@ class Ring:
 
 
 class RopeTable:
-    """Cached fp32 cos/sin [n_frames][grid_h][grid_w][P] built on the GPU."""
+    """Cached fp32 cos/sin [n_frames][grid_h][grid_w][P] built on the GPU for the
+    frames first_frame .. first_frame + n_frames - 1.
 
-    def __init__(self, g: B.Geom, n_frames: int, theta: float, device="cuda"):
+    The path reads only the rows of the chunk it processes, so a table of
+    chunk_frames frames, rebuilt in place for each chunk (`rebuild`), serves a
+    stream of any length in constant memory."""
+
+    def __init__(self, g: B.Geom, n_frames: int, theta: float, device="cuda",
+                 first_frame: int = 0):
         P = g.head_dim // 2
+        self.g, self.theta = g, theta
         self.n_frames = n_frames
         self.cos = torch.empty((n_frames, g.grid_h, g.grid_w, P), dtype=torch.float32,
                                device=device)
         self.sin = torch.empty_like(self.cos)
-        B.ust_rope_table_build(g, n_frames, theta, self.cos, self.sin)
+        self.rebuild(first_frame)
+
+    def rebuild(self, first_frame: int) -> None:
+        """Refill the same buffers with the rows of frames first_frame onward."""
+        B.ust_rope_table_build(self.g, self.n_frames, self.theta, self.cos, self.sin,
+                               first_frame=first_frame)
+        self.first_frame = first_frame
 
 
 @dataclass
@@ -236,20 +249,21 @@ def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
     value projections go through bufs.v and the full append."""
     if v_into_ring(wv, bufs):
         B.ust_kv_append(g, ring.abi, k_new, None, table.cos, table.sin,
-                        table.n_frames, frame_start)
+                        table.n_frames, frame_start, tab_first_frame=table.first_frame)
         B.ust_lowrank_proj_v_append(g, ring.abi, x, wv.a, wv.b, bufs.t_v, wv.k_in, wv.rank,
                                     frame_start)
     else:
         lowrank_apply(wv, x, bufs.v, bufs.t_v)
         B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,
-                        table.n_frames, frame_start)
+                        table.n_frames, frame_start, tab_first_frame=table.first_frame)
     if bufs.attn_work is not None:
         B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, table.n_frames,
                                 frame_start, n_recent, scale, bufs.o, bufs.lse,
-                                bufs.attn_work, 0)
+                                bufs.attn_work, 0, tab_first_frame=table.first_frame)
     else:
         B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames,
-                          frame_start, n_recent, scale, bufs.o, bufs.lse)
+                          frame_start, n_recent, scale, bufs.o, bufs.lse,
+                          tab_first_frame=table.first_frame)
     lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
     return bufs.y
 
@@ -263,14 +277,15 @@ def layer_chunk_fused(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
     and the output projection.  x: [NQ][hidden]; q_buf: [NQ][H*D]."""
     hidden = x.shape[1]
     B.ust_qkv_append(g, ring.abi, x, w_qkv, hidden, table.cos, table.sin, table.n_frames,
-                     frame_start, q_buf)
+                     frame_start, q_buf, tab_first_frame=table.first_frame)
     if bufs.attn_work is not None:
         B.ust_window_attn_split(g, ring.abi, q_buf, table.cos, table.sin, table.n_frames,
                                 frame_start, n_recent, scale, bufs.o, bufs.lse,
-                                bufs.attn_work, 0)
+                                bufs.attn_work, 0, tab_first_frame=table.first_frame)
     else:
         B.ust_window_attn(g, ring.abi, q_buf, table.cos, table.sin, table.n_frames,
-                          frame_start, n_recent, scale, bufs.o, bufs.lse)
+                          frame_start, n_recent, scale, bufs.o, bufs.lse,
+                          tab_first_frame=table.first_frame)
     lowrank_apply(wo, bufs.o, bufs.y, bufs.t_o)
     return bufs.y
 

@@ -118,14 +118,22 @@ typedef struct ust_kv {
 int32_t ust_v_row_len(int32_t tokens_per_frame);
 
 /* Build the cached RoPE coefficients (abstract: RoPE is applied from
- * precomputed coefficients).  For every frame f < n_frames, row y, column x and pair p,
+ * precomputed coefficients) for the frames first_frame .. first_frame +
+ * n_frames - 1.  For every such frame f, row y, column x and pair p,
  * angle = pos * theta^(-j/n) with (pos, j, n) given by p's axis as in
- * ust_geom; computed in fp64 and rounded to fp32.
- *   cos_out, sin_out: fp32 [n_frames][grid_h][grid_w][head_dim/2], written.
+ * ust_geom (pos = f, the absolute frame, on the temporal axis); computed in
+ * fp64 and rounded to fp32.  The consumers read only the rows of the
+ * chunk they process, so a table of one chunk's frames, built per chunk,
+ * serves a stream of any length; a table from frame 0 serves every chunk
+ * whose frames it covers.
+ *   cos_out, sin_out: fp32 [n_frames][grid_h][grid_w][head_dim/2], written;
+ *         row i holds frame first_frame + i.
  * Errors: NULL pointers; n_frames <= 0 or bad geometry (UST_E_SHAPE);
- * theta <= 0 (UST_E_RANGE); head_dim not 64/128 (UST_E_UNSUPPORTED). */
-ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double theta,
-                                float* cos_out, float* sin_out, hipStream_t stream);
+ * theta <= 0, first_frame < 0 or a frame past INT32_MAX (UST_E_RANGE);
+ * head_dim not 64/128 (UST_E_UNSUPPORTED). */
+ust_status ust_rope_table_build(const ust_geom* g, int32_t first_frame, int32_t n_frames,
+                                double theta, float* cos_out, float* sin_out,
+                                hipStream_t stream);
 
 /* Append one chunk to the KV ring (abstract: the KV cache and its indexing).
  * For every token n of the chunk (frame f = frame_start + n / T at (y, x))
@@ -137,16 +145,18 @@ ust_status ust_rope_table_build(const ust_geom* g, int32_t n_frames, double thet
  *   k_new, v_new: bf16 [chunk_frames*T][n_heads][head_dim], read.  v_new may
  *         be NULL: then only the keys are appended (the values reach the
  *         ring another way, e.g. ust_lowrank_proj_v_append).
- *   cos_tab, sin_tab: the table of ust_rope_table_build over n_tab_frames.
- * Errors: NULL k_new or table; frame_start < 0 or the chunk's frames not all
- * < n_tab_frames (UST_E_RANGE); n_slots - n_sink < chunk_frames or
- * n_sink < 0 (UST_E_RANGE); misaligned pointers; T not a multiple of 8 or
- * head_dim not 64/128 (UST_E_UNSUPPORTED). */
+ *   cos_tab, sin_tab: a table of ust_rope_table_build holding the frames
+ *         tab_first_frame .. tab_first_frame + n_tab_frames - 1; only the
+ *         chunk's own rows are read.
+ * Errors: NULL k_new or table; frame_start < 0, tab_first_frame < 0 or the
+ * chunk's frames not all in the table (UST_E_RANGE); n_slots - n_sink <
+ * chunk_frames or n_sink < 0 (UST_E_RANGE); misaligned pointers; T not a
+ * multiple of 8 or head_dim not 64/128 (UST_E_UNSUPPORTED). */
 ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv,
                          const void* k_new, const void* v_new,
                          const float* cos_tab, const float* sin_tab,
-                         int32_t n_tab_frames, int32_t frame_start,
-                         hipStream_t stream);
+                         int32_t tab_first_frame, int32_t n_tab_frames,
+                         int32_t frame_start, hipStream_t stream);
 
 /* Chunk-causal attention over the limited window (abstract: limited temporal
  * window in the KV cache; Table 3: chunks of three latent frames).
@@ -161,6 +171,9 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv,
  * Arithmetic: bf16 MFMA products with fp32 accumulation and fp32 softmax;
  * the rotated, scaled query and the probabilities are rounded to bf16.
  *   q:   bf16 [chunk_frames*T][n_heads][head_dim], un-rotated, read.
+ *   cos_tab, sin_tab, tab_first_frame, n_tab_frames: the table, as in
+ *        ust_kv_append (the rows of the chunk's frames rotate the queries;
+ *        the window's keys were rotated when they were appended).
  *   out: bf16, same layout, written.
  *   lse_opt: NULL, or fp32 [n_heads][chunk_frames*T]: ln sum_m exp(s_m).
  * Errors: as ust_kv_append, plus UST_E_RANGE when a window frame is no longer
@@ -169,7 +182,7 @@ ust_status ust_kv_append(const ust_geom* g, const ust_kv* kv,
  * UST_MAX_WINDOW_FRAMES frames; n_recent < -1 (UST_E_RANGE). */
 ust_status ust_window_attn(const ust_geom* g, const ust_kv* kv, const void* q,
                            const float* cos_tab, const float* sin_tab,
-                           int32_t n_tab_frames, int32_t frame_start,
+                           int32_t tab_first_frame, int32_t n_tab_frames, int32_t frame_start,
                            int32_t n_recent, float scale, void* out,
                            float* lse_opt, hipStream_t stream);
 
@@ -206,7 +219,8 @@ size_t ust_window_attn_work_bytes(const ust_geom* g, int32_t n_workgroups);
  * (UST_E_ALIGN), work_bytes too small or n_workgroups > 65536 (UST_E_SHAPE). */
 ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void* q,
                                  const float* cos_tab, const float* sin_tab,
-                                 int32_t n_tab_frames, int32_t frame_start,
+                                 int32_t tab_first_frame, int32_t n_tab_frames,
+                                 int32_t frame_start,
                                  int32_t n_recent, float scale, void* out,
                                  float* lse_opt, void* work, size_t work_bytes,
                                  int32_t n_workgroups, hipStream_t stream);
@@ -227,14 +241,17 @@ ust_status ust_window_attn_split(const ust_geom* g, const ust_kv* kv, const void
  *   x:     bf16 [chunk_frames*T][hidden], read.
  *   w_qkv: bf16 [3 * n_heads * head_dim][hidden], output-major: rows of W_q,
  *          then of W_k, then of W_v (row j = output feature j).  Read.
+ *   cos_tab, sin_tab, tab_first_frame, n_tab_frames: the table, as in
+ *          ust_kv_append.
  *   q_out: bf16 [chunk_frames*T][n_heads][head_dim], written.
  * Arithmetic: bf16 MFMA with fp32 accumulation.
  * Errors: as ust_kv_append; hidden <= 0 (UST_E_SHAPE), not a multiple of 64
  * (UST_E_UNSUPPORTED); operands past 32-bit indexing (UST_E_SHAPE). */
 ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
                           const void* w_qkv, int32_t hidden, const float* cos_tab,
-                          const float* sin_tab, int32_t n_tab_frames, int32_t frame_start,
-                          void* q_out, hipStream_t stream);
+                          const float* sin_tab, int32_t tab_first_frame,
+                          int32_t n_tab_frames, int32_t frame_start, void* q_out,
+                          hipStream_t stream);
 
 /* Low-rank projection Y = (X A_r) B_r (+ bias) (abstract: truncated SVD of
  * the attention value and output projections).

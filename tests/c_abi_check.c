@@ -98,14 +98,14 @@ int main(void) {
   const ust_kv ring = {k, v, N_SLOTS, N_SINK};
 
   /* argument errors: nothing is launched, a status and a message come back */
-  EXPECT(ust_window_attn(&g, &ring, NULL, cs, sn, NF, 0, N_RECENT, 0.f, o1, NULL, 0) == UST_E_NULL &&
+  EXPECT(ust_window_attn(&g, &ring, NULL, cs, sn, 0, NF, 0, N_RECENT, 0.f, o1, NULL, 0) == UST_E_NULL &&
              strlen(ust_last_error()) > 0, "NULL q not rejected");
-  EXPECT(ust_kv_append(&g, &ring, kn, vn, cs, sn, NF, NF - 2, 0) == UST_E_RANGE,
+  EXPECT(ust_kv_append(&g, &ring, kn, vn, cs, sn, 0, NF, NF - 2, 0) == UST_E_RANGE,
          "chunk past the table not rejected");
-  EXPECT(ust_window_attn_split(&g, &ring, q, cs, sn, NF, 0, N_RECENT, 0.f, o1, NULL, work,
+  EXPECT(ust_window_attn_split(&g, &ring, q, cs, sn, 0, NF, 0, N_RECENT, 0.f, o1, NULL, work,
                                work_bytes - 4, N_WG, 0) == UST_E_SHAPE, "small workspace not rejected");
 
-  UST_OK_(ust_rope_table_build(&g, NF, 10000.0, cs, sn, 0));
+  UST_OK_(ust_rope_table_build(&g, 0, NF, 10000.0, cs, sn, 0));
 
   uint16_t* hq = malloc(nc * 2);
   uint16_t* hk = malloc(nc * 2);
@@ -124,9 +124,9 @@ int main(void) {
       HIP_OK(hipMemcpy(q, hq, nc * 2, hipMemcpyHostToDevice));
       HIP_OK(hipMemcpy(kn, hk, nc * 2, hipMemcpyHostToDevice));
       HIP_OK(hipMemcpy(vn, hv, nc * 2, hipMemcpyHostToDevice));
-      UST_OK_(ust_kv_append(&g, &ring, kn, vn, cs, sn, NF, CF * c, 0));
-      UST_OK_(ust_window_attn(&g, &ring, q, cs, sn, NF, CF * c, N_RECENT, 0.f, o1, NULL, 0));
-      UST_OK_(ust_window_attn_split(&g, &ring, q, cs, sn, NF, CF * c, N_RECENT, 0.f, o2, NULL,
+      UST_OK_(ust_kv_append(&g, &ring, kn, vn, cs, sn, 0, NF, CF * c, 0));
+      UST_OK_(ust_window_attn(&g, &ring, q, cs, sn, 0, NF, CF * c, N_RECENT, 0.f, o1, NULL, 0));
+      UST_OK_(ust_window_attn_split(&g, &ring, q, cs, sn, 0, NF, CF * c, N_RECENT, 0.f, o2, NULL,
                                     work, work_bytes, N_WG, 0));
       HIP_OK(hipDeviceSynchronize());
       HIP_OK(hipMemcpy(h1, o1, nc * 2, hipMemcpyDeviceToHost));

@@ -83,6 +83,21 @@ def test_rope_table(name):
         assert np.all(np.abs(g - ref) <= ulp + 1e-300)
 
 
+@pytest.mark.parametrize("first", [9, 1_000_002, 2 ** 31 - 3])
+def test_rope_table_from_a_later_frame(first):
+    """A chunk's own table (3 frames from `first`, up to the last int32
+    frame) against the oracle's, within one fp32 ulp."""
+    w = wl.WAN_WINDOW
+    print(f"[rope_table from frame {first}]", flush=True)
+    t = P.RopeTable(_g(w), 3, w.theta, first_frame=first)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=first)
+    for got, ref in ((t.cos, c_ref), (t.sin, s_ref)):
+        g = got.cpu().numpy().astype(np.float64)
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(g - ref) <= ulp + 1e-300)
+
+
 # ------------------------------------------------------------------ KV append
 
 def _append_all(w, n_chunks=None, tokens=None):
@@ -142,23 +157,25 @@ def test_kv_append(name):
 
 # ------------------------------------------------------------------ attention
 
-def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True, n_wg=None):
+def _attn_gpu(g, w, ring, table, qb, c, n_recent=None, lse=True, n_wg=None, f0=None):
     """ust_window_attn, or ust_window_attn_split over n_wg workgroups (0: one
     per compute unit) with a NaN-filled workspace, so that a merge reading a
-    partial result nobody wrote shows up as NaN."""
+    partial result nobody wrote shows up as NaN.  The chunk starts at frame
+    f0 (default 3 c)."""
     q = P.to_device_bf16(qb)
     out = torch.empty_like(q)
     l = torch.empty((w.n_heads, w.n_q), dtype=torch.float32, device="cuda") if lse else None
     nr = w.n_recent if n_recent is None else n_recent
+    f0 = 3 * c if f0 is None else f0
     if n_wg is None:
-        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
-                          nr, 0.0, out, l)
+        B.ust_window_attn(g, ring.abi, q, table.cos, table.sin, table.n_frames, f0,
+                          nr, 0.0, out, l, tab_first_frame=table.first_frame)
     else:
         nbytes = B.ust_window_attn_work_bytes(g, n_wg)
         assert nbytes > 0 and nbytes % 4 == 0
         work = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
-        B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, w.n_tab_frames, 3 * c,
-                                nr, 0.0, out, l, work, n_wg)
+        B.ust_window_attn_split(g, ring.abi, q, table.cos, table.sin, table.n_frames, f0,
+                                nr, 0.0, out, l, work, n_wg, tab_first_frame=table.first_frame)
     torch.cuda.synchronize()
     return P.from_device_bf16(out), (l.cpu().numpy() if lse else None)
 
@@ -338,6 +355,85 @@ def test_streaming_far_past_one_clip():
             o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg)
             assert_close(_f64(o_gpu), o_ref, f"stream chunk {c} O")
             assert_close(lse_gpu, lse_ref, f"stream chunk {c} lse", max_abs=2e-2, rel_l2=1e-3)
+
+
+def test_stream_with_chunk_tables_equals_full_table():
+    """A stream of 8 chunks through a 12-slot ring, once with one table over
+    all 24 frames and once with a 3-frame table rebuilt in place for each
+    chunk: ring, outputs and log-sum-exps agree bit for bit, for the append,
+    both attention schedules and the fused projection's epilogue."""
+    w = wl.MID.replace(name="mid_tables", wid=31, n_chunks=8, n_tab_frames=24)
+    g = _g(w)
+    full = P.RopeTable(g, w.n_tab_frames, w.theta)
+    own = P.RopeTable(g, 3, w.theta)
+    rings = [P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS) for _ in range(2)]
+    rs = np.random.default_rng(71)
+    hidden = 256
+    w_qkv = P.to_device_bf16(wl.f32_to_bf16_bits(
+        rs.standard_normal((3 * w.n_heads * w.head_dim, hidden)) * hidden ** -0.5))
+    for c in range(w.n_chunks):
+        own.rebuild(3 * c)
+        kb = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_K, c))
+        vb = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_V, c))
+        qb = wl.chunk_tokens(w, wl.TAG_Q, c)
+        res = []
+        for ring, table in zip(rings, (full, own)):
+            B.ust_kv_append(g, ring.abi, kb, vb, table.cos, table.sin, table.n_frames, 3 * c,
+                            tab_first_frame=table.first_frame)
+            outs = [_attn_gpu(g, w, ring, table, qb, c, n_wg=n_wg) for n_wg in (None, 0)]
+            res.append((P.from_device_bf16(ring.k), P.from_device_bf16(ring.v), outs))
+        print(f"[chunk tables: chunk {c}]", flush=True)
+        (k1, v1, o1), (k2, v2, o2) = res
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2), f"chunk {c} ring"
+        for (a, la), (b, lb) in zip(o1, o2):
+            assert np.array_equal(a, b) and np.array_equal(la, lb), f"chunk {c} attention"
+    # the fused projection's epilogue rotates K with the same rows
+    x = P.to_device_bf16(wl.f32_to_bf16_bits(rs.standard_normal((w.n_q, hidden))))
+    c = w.n_chunks - 1
+    qs = []
+    for ring, table in zip(rings, (full, own)):
+        q_out = torch.empty((w.n_q, w.n_heads * w.head_dim), dtype=torch.bfloat16, device="cuda")
+        B.ust_qkv_append(g, ring.abi, x, w_qkv, hidden, table.cos, table.sin, table.n_frames,
+                         3 * c, q_out, tab_first_frame=table.first_frame)
+        qs.append(q_out)
+    torch.cuda.synchronize()
+    assert torch.equal(qs[0].view(torch.int16), qs[1].view(torch.int16))
+    for a, b in ((rings[0].k, rings[1].k), (rings[0].v, rings[1].v)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stream_a_million_frames_in():
+    """A stream a million frames in, with a table of the chunk's own three
+    frames for each chunk: the sink chunk (frames 0-2, its own table from
+    frame 0) and the chunks at frames F-6, F-3 and F (F = 1,000,002), then
+    the attention of the chunk at F on both schedules, against the oracle
+    fed the same tables, in full."""
+    w = wl.MID
+    g = _g(w)
+    F = 1_000_002
+    ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    table = P.RopeTable(g, 3, w.theta)
+    cache = O.KVCache(w.n_slots, w.n_heads, w.T, w.head_dim)
+    for c, f0 in enumerate((0, F - 6, F - 3, F)):
+        table.rebuild(f0)
+        cos, sin = O.rope_table(3, w.grid_h, w.grid_w, w.pairs, w.theta, first_frame=f0)
+        kb = wl.chunk_tokens(w, wl.TAG_K, c)
+        vb = wl.chunk_tokens(w, wl.TAG_V, c)
+        B.ust_kv_append(g, ring.abi, P.to_device_bf16(kb), P.to_device_bf16(vb), table.cos,
+                        table.sin, 3, f0, tab_first_frame=f0)
+        O.kv_append(cache, _f64(kb), _f64(vb), cos, sin, f0, 3, w.grid_h, w.grid_w,
+                    w.n_slots, w.n_sink, tab_first=f0)
+    frames, slots = B.ust_window_plan(g, ring.abi, F, w.n_recent)
+    assert frames == [0, 1, 2] + list(range(F - 6, F + 3))
+    assert slots == [O.slot_of_frame(f, w.n_slots, w.n_sink) for f in frames]
+    qb = wl.chunk_tokens(w, wl.TAG_Q, 3)
+    o_ref, lse_ref = O.window_attn(cache, _f64(qb), cos, sin, F, 3, w.grid_h, w.grid_w,
+                                   w.n_slots, w.n_sink, w.n_recent, tab_first=F)
+    for n_wg in (None, 0):
+        print(f"[stream at frame {F} n_wg {n_wg}]", flush=True)
+        o_gpu, lse_gpu = _attn_gpu(g, w, ring, table, qb, 3, n_wg=n_wg, f0=F)
+        assert_close(_f64(o_gpu), o_ref, f"frame {F} O")
+        assert_close(lse_gpu, lse_ref, f"frame {F} lse", max_abs=2e-2, rel_l2=1e-3)
 
 
 def test_nan_outside_window_and_determinism():

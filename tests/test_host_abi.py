@@ -167,10 +167,10 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     ring = B.Kv(fake, fake, 21, 3)
     gp, rp = ctypes.byref(g), ctypes.byref(ring)
     # NULL pointers
-    assert _raw(lib, "ust_kv_append", gp, rp, None, fake, fake, fake, 21, 0, None)[0] == "UST_E_NULL"
-    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 0, 6, 0.0, None, None,
+    assert _raw(lib, "ust_kv_append", gp, rp, None, fake, fake, fake, 0, 21, 0, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 0, 21, 0, 6, 0.0, None, None,
                 None)[0] == "UST_E_NULL"
-    assert _raw(lib, "ust_rope_table_build", gp, 21, 1e4, None, fake, None)[0] == "UST_E_NULL"
+    assert _raw(lib, "ust_rope_table_build", gp, 0, 21, 1e4, None, fake, None)[0] == "UST_E_NULL"
     assert _raw(lib, "ust_lowrank_proj", fake, fake, fake, None, None, fake, 8, 8, 8, 8,
                 None)[0] == "UST_E_NULL"
     assert _raw(lib, "ust_lowrank_proj_static", None, fake, fake, None, fake, 8, 8, 8, 8,
@@ -204,11 +204,11 @@ def test_compute_entry_points_reject_bad_arguments(lib):
     assert _raw(lib, "ust_conv3d_causal_stream", fake, fake, None, fake, 63, 512, 1024, 32, 32,
                 None)[0] == "UST_E_SHAPE"
     # frames outside the table
-    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 21, 19, None)[0] == "UST_E_RANGE"
-    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake, None,
+    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, 0, 21, 19, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, 0, 21, 21, 6, 0.0, fake, None,
                 None)[0] == "UST_E_RANGE"
     # misaligned
-    assert _raw(lib, "ust_kv_append", gp, rp, fake + 2, fake, fake, fake, 21, 0, None)[0] == "UST_E_ALIGN"
+    assert _raw(lib, "ust_kv_append", gp, rp, fake + 2, fake, fake, fake, 0, 21, 0, None)[0] == "UST_E_ALIGN"
     assert _raw(lib, "ust_lowrank_proj", fake, fake, None, None, None, fake, 8, 12, 8, 8,
                 None)[0] == "UST_E_ALIGN"
     # shapes
@@ -216,28 +216,63 @@ def test_compute_entry_points_reject_bad_arguments(lib):
                 None)[0] == "UST_E_SHAPE"
     assert _raw(lib, "ust_lowrank_proj", fake, fake, None, None, None, fake, 0, 16, 8, 8,
                 None)[0] == "UST_E_SHAPE"
-    assert _raw(lib, "ust_rope_table_build", gp, 0, 1e4, fake, fake, None)[0] == "UST_E_SHAPE"
-    assert _raw(lib, "ust_rope_table_build", gp, 4, -1.0, fake, fake, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_rope_table_build", gp, 0, 0, 1e4, fake, fake, None)[0] == "UST_E_SHAPE"
+    assert _raw(lib, "ust_rope_table_build", gp, 0, 4, -1.0, fake, fake, None)[0] == "UST_E_RANGE"
     # unsupported head size and token count
     g2 = cvd.geom(30, 52, 12, 96, 16, 16, 16, 3)
-    assert _raw(lib, "ust_kv_append", ctypes.byref(g2), rp, fake, fake, fake, fake, 21, 0,
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g2), rp, fake, fake, fake, fake, 0, 21, 0,
                 None)[0] == "UST_E_UNSUPPORTED"
     g3 = cvd.geom(3, 5, 12, 128, 22, 21, 21, 3)
-    assert _raw(lib, "ust_kv_append", ctypes.byref(g3), rp, fake, fake, fake, fake, 21, 0,
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g3), rp, fake, fake, fake, fake, 0, 21, 0,
                 None)[0] == "UST_E_UNSUPPORTED"
     # pair split that does not add up
     g4 = cvd.geom(30, 52, 12, 128, 22, 21, 20, 3)
-    assert _raw(lib, "ust_kv_append", ctypes.byref(g4), rp, fake, fake, fake, fake, 21, 0,
+    assert _raw(lib, "ust_kv_append", ctypes.byref(g4), rp, fake, fake, fake, fake, 0, 21, 0,
                 None)[0] == "UST_E_SHAPE"
     # ring that cannot hold a chunk
     small = B.Kv(fake, fake, 4, 3)
-    assert _raw(lib, "ust_kv_append", gp, ctypes.byref(small), fake, fake, fake, fake, 21, 6,
+    assert _raw(lib, "ust_kv_append", gp, ctypes.byref(small), fake, fake, fake, fake, 0, 21, 6,
                 None)[0] == "UST_E_RANGE"
     # a window frame already overwritten
     ring10 = B.Kv(fake, fake, 10, 3)
-    st, msg = _raw(lib, "ust_window_attn", gp, ctypes.byref(ring10), fake, fake, fake, 21, 15,
+    st, msg = _raw(lib, "ust_window_attn", gp, ctypes.byref(ring10), fake, fake, fake, 0, 21, 15,
                    6, 0.0, fake, None, None)
     assert st == "UST_E_RANGE" and "no longer in the ring" in msg
+
+
+def test_table_first_frame_rejects_bad_arguments(lib):
+    """A table holds the frames tab_first_frame .. tab_first_frame + n_tab_frames
+    - 1: the chunk's frames must all lie there, in every consumer; the builder
+    rejects a negative first frame and frames past INT32_MAX.  Every call here
+    fails in validation, before any launch."""
+    w = wl.WAN_WINDOW
+    g = _geom(w)
+    fake = 0x10000
+    ring = B.Kv(fake, fake, 21, 3)
+    gp, rp = ctypes.byref(g), ctypes.byref(ring)
+    imax = 2 ** 31 - 1
+    assert _raw(lib, "ust_rope_table_build", gp, -1, 3, 1e4, fake, fake, None)[0] == "UST_E_RANGE"
+    st, msg = _raw(lib, "ust_rope_table_build", gp, imax - 1, 3, 1e4, fake, fake, None)
+    assert st == "UST_E_RANGE" and "INT32_MAX" in msg
+    kv = lambda t0, n_tab, f0: _raw(lib, "ust_kv_append", gp, rp, fake, fake, fake, fake, t0,
+                                    n_tab, f0, None)
+    assert kv(-1, 21, 0)[0] == "UST_E_RANGE"
+    assert kv(3, 3, 0)[0] == "UST_E_RANGE"                 # chunk before the table
+    assert kv(100000, 2, 100000)[0] == "UST_E_RANGE"       # last chunk frame past the table
+    st, msg = kv(100000, 3, 100001)
+    assert st == "UST_E_RANGE" and "100000..100002" in msg
+    # frames near INT32_MAX: 64-bit bounds, no wrap
+    assert kv(imax - 2, 3, imax - 1)[0] == "UST_E_RANGE"
+    att = lambda t0, n_tab, f0: _raw(lib, "ust_window_attn", gp, rp, fake, fake, fake, t0, n_tab,
+                                     f0, 6, 0.0, fake, None, None)
+    assert att(-3, 21, 0)[0] == "UST_E_RANGE"
+    assert att(16, 3, 15)[0] == "UST_E_RANGE"
+    assert att(15, 2, 15)[0] == "UST_E_RANGE"
+    need = lib.ust_window_attn_work_bytes(gp, 256)
+    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 18, 3, 15, 6, 0.0, fake,
+                None, fake, need, 256, None)[0] == "UST_E_RANGE"
+    assert _raw(lib, "ust_qkv_append", gp, rp, fake, fake, 1536, fake, fake, 9, 3, 6, fake,
+                None)[0] == "UST_E_RANGE"
 
 
 def test_window_attn_split_rejects_bad_arguments(lib):
@@ -249,11 +284,11 @@ def test_window_attn_split_rejects_bad_arguments(lib):
     ring = B.Kv(fake, fake, 21, 3)
     gp, rp = ctypes.byref(g), ctypes.byref(ring)
     need = lib.ust_window_attn_work_bytes(gp, 256)
-    args = (gp, rp, fake, fake, fake, 21, 15, 6, 0.0, fake, None)
+    args = (gp, rp, fake, fake, fake, 0, 21, 15, 6, 0.0, fake, None)
     # the same validation as the unsplit call comes first
-    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 21, 21, 6, 0.0, fake,
+    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 0, 21, 21, 6, 0.0, fake,
                 None, fake, need, 256, None)[0] == "UST_E_RANGE"
-    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 21, 15, 6, 0.0, None,
+    assert _raw(lib, "ust_window_attn_split", gp, rp, fake, fake, fake, 0, 21, 15, 6, 0.0, None,
                 None, fake, need, 256, None)[0] == "UST_E_NULL"
     # then the workspace
     assert _raw(lib, "ust_window_attn_split", *args, None, need, 256, None)[0] == "UST_E_NULL"
@@ -272,7 +307,7 @@ def test_qkv_append_rejects_bad_arguments(lib):
     ring = B.Kv(fake, fake, 21, 3)
     gp, rp = ctypes.byref(g), ctypes.byref(ring)
     call = lambda x, wq, hidden, n_tab, f0, q: _raw(lib, "ust_qkv_append", gp, rp, x, wq, hidden,
-                                                     fake, fake, n_tab, f0, q, None)
+                                                     fake, fake, 0, n_tab, f0, q, None)
     assert call(None, fake, 1536, 21, 0, fake)[0] == "UST_E_NULL"
     assert call(fake, fake, 1536, 21, 0, None)[0] == "UST_E_NULL"
     assert call(fake + 8, fake, 1536, 21, 0, fake)[0] == "UST_E_ALIGN"
@@ -280,7 +315,7 @@ def test_qkv_append_rejects_bad_arguments(lib):
     assert call(fake, fake, 1560, 21, 0, fake)[0] == "UST_E_UNSUPPORTED"   # 1560 % 64 = 24
     assert call(fake, fake, 1536, 21, 19, fake)[0] == "UST_E_RANGE"     # frames 19..21
     small = B.Kv(fake, fake, 4, 3)
-    assert _raw(lib, "ust_qkv_append", gp, ctypes.byref(small), fake, fake, 1536, fake, fake,
+    assert _raw(lib, "ust_qkv_append", gp, ctypes.byref(small), fake, fake, 1536, fake, fake, 0,
                 21, 6, fake, None)[0] == "UST_E_RANGE"
 
 
@@ -305,7 +340,7 @@ def test_lowrank_proj_v_append_rejects_bad_arguments(lib):
     assert call(fake, fake, 1536, 512, -3)[0] == "UST_E_RANGE"
     small = B.Kv(fake, fake, 4, 3)
     assert call(fake, fake, 1536, 512, 6, ctypes.byref(small))[0] == "UST_E_RANGE"
-    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake + 2, fake, fake, 21, 0,
+    assert _raw(lib, "ust_kv_append", gp, rp, fake, fake + 2, fake, fake, 0, 21, 0,
                 None)[0] == "UST_E_ALIGN"
 
 
