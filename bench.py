@@ -46,8 +46,11 @@ METRIC = ("windowed chunk-attn TFLOP/s + µs per layer-chunk (Wan-1.3B shape), "
 # the figure only while the sources still hash the same (null otherwise).
 ATTN_SOURCES = ("window_attn.hip", "attn_schedule.h", "ust_device.h")
 ATTN_TRAFFIC = {
-    ("wan_window", "whole"): {"src_sha16": "5c8fcf3a7ae9e2c9",
-                              "bytes": (2 * 108170 + 17700) * 1024},
+    ("wan_window", "whole"): {"src_sha16": "cf5e64c3889d6500",
+                              "bytes": (2 * 108159 + 17698) * 1024},
+    # the split schedule: the attention and the merge kernel together
+    ("wan_720p", "split"): {"src_sha16": "cf5e64c3889d6500",
+                            "bytes": (2 * (588995 + 17004) + 62660 + 204) * 1024},
 }
 # the decoder convolution, per workload, same scaling and keying
 CONV_SOURCES = ("conv3d.hip", "ust_device.h")
