@@ -356,9 +356,11 @@ def sample_chunk(dit, x_init: np.ndarray, noises: Sequence[np.ndarray],
 
 def rne_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bfloat16 (ties to even), returned
-    as float64.  Used to build a cache whose keys are stored in bfloat16.
-    Normal range only (|x| >= 2**-126); bfloat16 subnormals do not occur in
-    the workloads."""
+    as float64: the rounding every test input goes through.  The seeded
+    input generator rounds float32 to bfloat16 by integer bit arithmetic;
+    this is the same rounding by another route (frexp and round-half-even),
+    and the pins compare the two.  Normal range only (|x| >= 2**-126);
+    bfloat16 subnormals do not occur in the workloads."""
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)                  # x = m * 2**e, 0.5 <= |m| < 1
     # bfloat16 keeps 8 significant bits: scale the mantissa to [128, 256)
