@@ -75,7 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         I32, P]),
         "ust_qkv_append": (I32, [GP, KP, P, P, I32, P, P, I32, I32, I32, P, P]),
         "ust_lowrank_proj": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, P]),
-        "ust_lowrank_proj_v_append": (I32, [GP, KP, P, P, P, P, I32, I32, I32, P]),
+        "ust_lowrank_proj_v_append": (I32, [GP, KP, P, P, P, P, I32, I32, P, P, P, I32, I32, I32,
+                                            P]),
         "ust_lowrank_proj_static": (I32, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "ust_conv3d_causal": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
         "ust_conv3d_causal_stream": (I32, [P, P, P, P, I32, I32, I32, I32, I32, P]),
@@ -186,10 +187,14 @@ def ust_qkv_append(g: Geom, ring: Kv, x, w_qkv, hidden: int, cos_tab, sin_tab,
 
 
 def ust_lowrank_proj_v_append(g: Geom, ring: Kv, x, a, b, t_work, hidden: int, rank: int,
-                              frame_start: int, stream=None) -> None:
+                              frame_start: int, stream=None, k_new=None, cos_tab=None,
+                              sin_tab=None, n_tab_frames: int = 0,
+                              tab_first_frame: int = 0) -> None:
+    """k_new and the table (keyword arguments here) also append the keys."""
     _check(load().ust_lowrank_proj_v_append(ctypes.byref(g), ctypes.byref(ring), _ptr(x), _ptr(a),
-                                            _ptr(b), _ptr(t_work), hidden, rank, frame_start,
-                                            _stream(stream)))
+                                            _ptr(b), _ptr(t_work), hidden, rank, _ptr(k_new),
+                                            _ptr(cos_tab), _ptr(sin_tab), tab_first_frame,
+                                            n_tab_frames, frame_start, _stream(stream)))
 
 
 def ust_lowrank_proj(x, a, b, bias, t_work, y, M: int, K: int, r: int, N: int,

@@ -16,6 +16,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "append_keys.h"
 #include "gemm_order.h"
 #include "ust_device.h"
 #include "ust_internal.h"
@@ -25,6 +26,7 @@ namespace {
 
 constexpr int kBN = 128;
 constexpr int kBK = 64;
+constexpr int kKeysPerWg = 4;   // key tiles per key-append workgroup of the pipelined GEMM
 
 template <int MB>  // 32-row blocks of X per wave; BM = 64 * MB
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -201,10 +203,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // QKV: the fused Q/K/V projection epilogue (QkvEpilogue) instead of Y.
 // WM x WN waves (4 or 8); with 8, two waves share each SIMD, so one wave's
 // load-issue stalls are covered by the other's MFMAs.
-template <int BM, int BN, int STAGES, bool QKV, int WM, int WN>
+// KEYD (64 or 128, the head size; 0: none): workgroups past the product's
+// tiles rotate and append a chunk's keys (ka, append_keys.h), four key tiles
+// each, on the compute units the product leaves idle.
+template <int BM, int BN, int STAGES, bool QKV, int WM, int WN, int KEYD = 0>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
-gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
+gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e, AppendArgs ka) {
   constexpr int NW = WM * WN;
   constexpr int NT = 64 * NW;
   constexpr int MB = BM / (32 * WM);       // 32-row blocks of X per wave
@@ -230,6 +235,18 @@ gemm_nt_dma_kernel(GemmArgs g, QkvEpilogue e) {
   const int wm = wave % WM, wn = wave / WM;
   const int nbn = (g.N + BN - 1) / BN;
   const int nbm = (g.M + BM - 1) / BM;
+  if constexpr (KEYD != 0) {
+    // the launch's workgroups past the product's tiles append keys; the
+    // branch is uniform over the workgroup and comes before any barrier
+    constexpr int TPT = NT / kKeysPerWg;     // threads per key tile
+    const int ntile = nbm * nbn;
+    if (int(blockIdx.x) >= ntile) {
+      const int pos = xcd_range_pos(blockIdx.x, ntile, gridDim.x);
+      const int w = pos * kKeysPerWg + tid / TPT;
+      if (w < key_tiles(ka.T, ka.C, ka.H)) append_key_tile<KEYD, TPT>(ka, w, tid % TPT);
+      return;
+    }
+  }
   // XCD-aware tile order, row-major or grouped (gemm_order.h)
   const GemmTile tl = gemm_tile(blockIdx.x, nbm, nbn, int64_t(g.N) * g.K * 2);
   const int m0 = tl.m_blk * BM;
@@ -531,30 +548,55 @@ hipError_t launch_qkv_append(const GemmArgs& g, const QkvEpilogue& e, hipStream_
   // one head per output tile: the tile's feature width is the head size
   if (e.D == 128) {
     dim3 grid(((g.M + 255) / 256) * (g.N / 128));
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, true, 4, 2>), grid, dim3(512), 0, s, g, e);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, true, 4, 2>), grid, dim3(512), 0, s, g, e,
+                       AppendArgs{});
   } else {
     dim3 grid(((g.M + 191) / 192) * (g.N / 64));
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, true, 2, 2>), grid, dim3(256), 0, s, g, e);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<192, 64, 4, true, 2, 2>), grid, dim3(256), 0, s, g, e,
+                       AppendArgs{});
   }
   return hipGetLastError();
 }
 
+bool gemm_nt_pipelined(const GemmArgs& g) {
+  return g.K % 64 == 0 && int64_t(g.M) * g.K < (int64_t(1) << 31) &&
+         int64_t(g.N) * g.K < (int64_t(1) << 31);
+}
+
+namespace {
+
+// the pipelined kernel for this shape, with key_wgs key-append workgroups
+// after its tiles (KEYD = head size, 0 for none)
+template <int KEYD>
+void launch_pipelined(const GemmArgs& g, const AppendArgs& ka, int key_wgs, hipStream_t s) {
+  // narrow outputs (the rank-r factor product) get 128 x 128 tiles (148
+  // workgroups at 4680 x 512), wide ones 256 x 128 (228 at 4680 x 1536):
+  // one round on 256 CUs, 8 waves each
+  const QkvEpilogue none{};
+  if (g.N <= 768) {
+    dim3 grid(((g.M + 127) / 128) * ((g.N + 127) / 128) + key_wgs);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<128, 128, 3, false, 4, 2, KEYD>), grid, dim3(512), 0, s,
+                       g, none, ka);
+  } else {
+    dim3 grid(((g.M + 255) / 256) * ((g.N + 127) / 128) + key_wgs);
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, false, 4, 2, KEYD>), grid, dim3(512), 0, s,
+                       g, none, ka);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt_keys(const GemmArgs& g, const AppendArgs& ka, hipStream_t s) {
+  if (!gemm_nt_pipelined(g)) return hipErrorInvalidValue;
+  const int key_wgs = (key_tiles(ka.T, ka.C, ka.H) + kKeysPerWg - 1) / kKeysPerWg;
+  if (ka.D == 128) launch_pipelined<128>(g, ka, key_wgs, s);
+  else launch_pipelined<64>(g, ka, key_wgs, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s) {
-  if (g.K % 64 == 0 && int64_t(g.M) * g.K < (int64_t(1) << 31) &&
-      int64_t(g.N) * g.K < (int64_t(1) << 31)) {
-    // narrow outputs (the rank-r factor product) get 128 x 128 tiles (148
-    // workgroups at 4680 x 512), wide ones 256 x 128 (228 at 4680 x 1536):
-    // one round on 256 CUs, 8 waves each
-    const QkvEpilogue none{};
-    if (g.N <= 768) {
-      dim3 grid(((g.M + 127) / 128) * ((g.N + 127) / 128));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<128, 128, 3, false, 4, 2>), grid, dim3(512), 0, s, g,
-                         none);
-    } else {
-      dim3 grid(((g.M + 255) / 256) * ((g.N + 127) / 128));
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<256, 128, 3, false, 4, 2>), grid, dim3(512), 0, s, g,
-                         none);
-    }
+  if (gemm_nt_pipelined(g)) {
+    launch_pipelined<0>(g, AppendArgs{}, 0, s);
     return hipGetLastError();
   }
   const int nbn = (g.N + kBN - 1) / kBN;

@@ -1,5 +1,6 @@
-// Tile order of the pipelined GEMM: which output tile a workgroup computes.
-// Host and device share this code; it touches no memory.
+// Tile order of the pipelined GEMM: which output tile a workgroup computes,
+// and the order of the extra workgroups a launch may carry beyond its
+// tiles.  Host and device share this code; it touches no memory.
 //
 // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8), so XCD x receives workgroups x, x + 8, x + 16, ...; each XCD is
@@ -41,6 +42,21 @@ __host__ __device__ inline GemmTile gemm_tile(int b, int nbm, int nbn, int64_t w
   const int rows = nbm - first < kGroupRows ? nbm - first : kGroupRows;
   const int local = tile - grp * kGroupRows * nbn;
   return GemmTile{first + local % rows, local / rows};
+}
+
+// Position of workgroup b in the range [lo, hi) of a grid (lo <= b < hi)
+// when the range's workgroups are dealt to the XCDs in contiguous runs of
+// positions: XCD x's workgroups of the range, in dispatch order, take the
+// next positions of run x, and run x follows runs 0 .. x-1.
+__host__ __device__ inline int xcd_range_pos(int b, int lo, int hi) {
+  const int x = b & 7;
+  int start = 0;
+  for (int y = 0; y < x; ++y) {
+    const int first = lo + ((y - lo) % 8 + 8) % 8;   // the range's first workgroup on XCD y
+    start += first < hi ? (hi - 1 - first) / 8 + 1 : 0;
+  }
+  const int firstx = lo + ((x - lo) % 8 + 8) % 8;
+  return start + (b - firstx) / 8;
 }
 
 }  // namespace ust

@@ -16,6 +16,7 @@
 // ordered head-fastest and XCD-aware, so the table rows of a token tile are
 // fetched from HBM once and re-read by its other heads from the same L2.
 
+#include "append_keys.h"
 #include "ust_device.h"
 #include "ust_internal.h"
 
@@ -86,9 +87,9 @@ kv_append_kernel(AppendArgs a) {
       uint32_t kout[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_lo(kin[e]);
-        const float x1 = bf16_hi(kin[e]);
-        kout[e] = pack_bf16x2(x0 * c4[e] - x1 * s4[e], x0 * s4[e] + x1 * c4[e]);
+        float r0, r1;
+        rope_pair(bf16_lo(kin[e]), bf16_hi(kin[e]), c4[e], s4[e], r0, r1);
+        kout[e] = pack_bf16x2(r0, r1);
       }
       *reinterpret_cast<uint4*>(kdst + int64_t(tl) * D + dc * 8) =
           make_uint4(kout[0], kout[1], kout[2], kout[3]);

@@ -432,7 +432,10 @@ ust_status ust_qkv_append(const ust_geom* g, const ust_kv* kv, const void* x,
 
 ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const void* x,
                                      const void* a, const void* b, void* t_work, int32_t hidden,
-                                     int32_t rank, int32_t frame_start, hipStream_t stream) {
+                                     int32_t rank, const void* k_new, const float* cos_tab,
+                                     const float* sin_tab, int32_t tab_first_frame,
+                                     int32_t n_tab_frames, int32_t frame_start,
+                                     hipStream_t stream) {
   try {
     ust_status s = check_geom(g);
     if (s != UST_OK) return s;
@@ -441,7 +444,10 @@ ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const 
     s = check_ring_size(g, kv);
     if (s != UST_OK) return s;
     if (!x || !a || !b || !t_work) return fail(UST_E_NULL, "x, a, b or t_work is NULL");
-    if (!aligned16(x) || !aligned16(a) || !aligned16(b) || !aligned16(t_work))
+    if (k_new && (!cos_tab || !sin_tab))
+      return fail(UST_E_NULL, "k_new is given without the table");
+    if (!aligned16(x) || !aligned16(a) || !aligned16(b) || !aligned16(t_work) ||
+        (k_new && (!aligned16(k_new) || !aligned16(cos_tab) || !aligned16(sin_tab))))
       return fail(UST_E_ALIGN, "pointers must be 16-byte aligned");
     if (hidden <= 0 || rank <= 0)
       return fail(UST_E_SHAPE, "hidden %d and rank %d must be positive", hidden, rank);
@@ -457,8 +463,10 @@ ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const 
         int64_t(rank) * hidden >= (int64_t(1) << 31) || int64_t(N) * rank >= (int64_t(1) << 31))
       return fail(UST_E_SHAPE, "operands too large for 32-bit indexing");
     ust::QkvEpilogue e{};
-    // no table: the values are not rotated
-    s = chunk_slots(g, kv, 0, INT32_MAX, frame_start, e.chunk_slot);
+    // the values are not rotated: the table bounds the frames only when the
+    // keys come along
+    if (k_new) s = chunk_slots(g, kv, tab_first_frame, n_tab_frames, frame_start, e.chunk_slot);
+    else s = chunk_slots(g, kv, 0, INT32_MAX, frame_start, e.chunk_slot);
     if (s != UST_OK) return s;
     e.v_cache = static_cast<uint16_t*>(kv->v);
     e.T = T;
@@ -470,7 +478,33 @@ ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const 
     uint16_t* t = static_cast<uint16_t*>(t_work);
     const ust::GemmArgs g1{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(a),
                            nullptr, t, M, rank, hidden};
-    hipError_t err = ust::launch_gemm_nt(g1, stream);
+    hipError_t err;
+    if (k_new) {
+      // the keys' RoPE and append, as ust_kv_append with v_new NULL
+      ust::AppendArgs ka{};
+      for (int i = 0; i < g->chunk_frames; ++i) ka.chunk_slot[i] = e.chunk_slot[i];
+      ka.k_new = static_cast<const uint16_t*>(k_new);
+      ka.cos_tab = cos_tab;
+      ka.sin_tab = sin_tab;
+      ka.k_cache = static_cast<uint16_t*>(kv->k);
+      ka.T = T;
+      ka.TV = ust_v_row_len(T);
+      ka.H = g->n_heads;
+      ka.D = g->head_dim;
+      ka.C = g->chunk_frames;
+      ka.tab_frame = frame_start - tab_first_frame;
+      ka.with_v = 0;
+      // in the first product's launch where its kernel takes extra
+      // workgroups, else as a launch of its own before it
+      if (ust::gemm_nt_pipelined(g1)) {
+        err = ust::launch_gemm_nt_keys(g1, ka, stream);
+      } else {
+        err = ust::launch_kv_append(ka, stream);
+        if (err == hipSuccess) err = ust::launch_gemm_nt(g1, stream);
+      }
+    } else {
+      err = ust::launch_gemm_nt(g1, stream);
+    }
     if (err != hipSuccess) return hip_status(err, "lowrank_proj_v_append launch (X A)");
     const ust::GemmArgs g2{t, static_cast<const uint16_t*>(b), nullptr, nullptr, M, N, rank};
     return hip_status(ust::launch_qkv_append(g2, e, stream), "lowrank_proj_v_append launch (T B)");

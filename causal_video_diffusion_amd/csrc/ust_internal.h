@@ -113,6 +113,12 @@ hipError_t launch_window_attn(const AttnArgs& a, hipStream_t s);
 // workspace bytes of the key-split schedule over n_wg workgroups
 size_t window_attn_work_bytes(int32_t head_dim, int32_t n_wg);
 hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t s);
+// Whether launch_gemm_nt runs the pipelined kernel for this shape.
+bool gemm_nt_pipelined(const GemmArgs& a);
+// launch_gemm_nt's pipelined product with the keys of ka (with_v 0) rotated
+// and appended by extra workgroups of the same launch; for shapes where
+// gemm_nt_pipelined holds (hipErrorInvalidValue otherwise, nothing launched).
+hipError_t launch_gemm_nt_keys(const GemmArgs& a, const AppendArgs& ka, hipStream_t s);
 // bf16 elements of the device scratch behind ust_lowrank_proj_static
 constexpr size_t kLowrankScratchElems = size_t(UST_LOWRANK_STATIC_MAX_ELEMS);
 // that scratch's address on the current device (looked up once per device)

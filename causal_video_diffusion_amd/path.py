@@ -244,14 +244,15 @@ def layer_chunk(g: B.Geom, ring: Ring, table: RopeTable, x: torch.Tensor,
     x: hidden states [NQ][hidden]; q, k_new: [NQ][H*D] un-rotated (from the
     dense query/key projections).  The attention runs on the key-split
     schedule when bufs holds its workspace.  A truncated-SVD value projection
-    whose rank is a multiple of 64 stores V straight into the ring
-    (ust_lowrank_proj_v_append) and the append moves the keys only; other
-    value projections go through bufs.v and the full append."""
+    whose rank is a multiple of 64 stores V straight into the ring, and the
+    keys' RoPE and append ride in its first product's launch
+    (ust_lowrank_proj_v_append with k_new); other value projections go
+    through bufs.v and the full append."""
     if v_into_ring(wv, bufs):
-        B.ust_kv_append(g, ring.abi, k_new, None, table.cos, table.sin,
-                        table.n_frames, frame_start, tab_first_frame=table.first_frame)
         B.ust_lowrank_proj_v_append(g, ring.abi, x, wv.a, wv.b, bufs.t_v, wv.k_in, wv.rank,
-                                    frame_start)
+                                    frame_start, k_new=k_new, cos_tab=table.cos,
+                                    sin_tab=table.sin, n_tab_frames=table.n_frames,
+                                    tab_first_frame=table.first_frame)
     else:
         lowrank_apply(wv, x, bufs.v, bufs.t_v)
         B.ust_kv_append(g, ring.abi, k_new, bufs.v, table.cos, table.sin,

@@ -281,22 +281,34 @@ ust_status ust_lowrank_proj(const void* x, const void* a, const void* b,
  * f = frame_start + n / T) and head h,
  *   kv.v[slot(f)][h][:][n % T] = bf16_rne((x[n] A_r) B_r)[h][:]
  * with T rounded to bf16 between the two products, bit for bit the values
- * that ust_lowrank_proj followed by ust_kv_append would store.  The keys
- * are not touched (ust_kv_append with v_new NULL appends them).
+ * that ust_lowrank_proj followed by ust_kv_append would store.
+ * With k_new given, the chunk's keys are rotated and appended too, bit for
+ * bit as ust_kv_append with v_new NULL stores them; where the first
+ * product's kernel allows (hidden a multiple of 64), extra workgroups of
+ * its launch do it on the compute units the product leaves idle, otherwise
+ * a launch of its own precedes it.  With k_new NULL the keys are not
+ * touched (ust_kv_append with v_new NULL appends them).
  *   x:      bf16 [chunk_frames*T][hidden], read.
  *   a:      bf16 [rank][hidden], A_r output-major.  Read.
  *   b:      bf16 [n_heads*head_dim][rank], B_r output-major.  Read.
  *   t_work: bf16 [chunk_frames*T][rank] scratch, caller-owned (contents
  *           unspecified after the call).
- * Errors: NULL pointers; non-positive hidden or rank (UST_E_SHAPE); hidden
- * not a multiple of 8 or misaligned pointers (UST_E_ALIGN); rank not a
- * multiple of 64, T not a multiple of 8 or head_dim not 64/128
- * (UST_E_UNSUPPORTED); frame_start < 0 or a ring that cannot hold the chunk
- * (UST_E_RANGE); operands past 32-bit indexing (UST_E_SHAPE). */
+ *   k_new:  NULL, or bf16 [chunk_frames*T][n_heads][head_dim], the chunk's
+ *           un-rotated keys.  Read.
+ *   cos_tab, sin_tab, tab_first_frame, n_tab_frames: the RoPE table, as in
+ *           ust_kv_append; unused (may be NULL) when k_new is NULL.
+ * Errors: NULL pointers (the table too when k_new is given); non-positive
+ * hidden or rank (UST_E_SHAPE); hidden not a multiple of 8 or misaligned
+ * pointers (UST_E_ALIGN); rank not a multiple of 64, T not a multiple of 8
+ * or head_dim not 64/128 (UST_E_UNSUPPORTED); frame_start < 0, a ring that
+ * cannot hold the chunk, or, with k_new, the chunk's frames outside the
+ * table (UST_E_RANGE); operands past 32-bit indexing (UST_E_SHAPE). */
 ust_status ust_lowrank_proj_v_append(const ust_geom* g, const ust_kv* kv, const void* x,
                                      const void* a, const void* b, void* t_work,
-                                     int32_t hidden, int32_t rank, int32_t frame_start,
-                                     hipStream_t stream);
+                                     int32_t hidden, int32_t rank, const void* k_new,
+                                     const float* cos_tab, const float* sin_tab,
+                                     int32_t tab_first_frame, int32_t n_tab_frames,
+                                     int32_t frame_start, hipStream_t stream);
 
 /* Largest M * r that ust_lowrank_proj_static accepts: the bf16 elements of
  * its device scratch (8 MiB). */

@@ -11,6 +11,8 @@
 //    row blocks, span at most 2 kGroupRows row blocks and 32 / kGroupRows +
 //    2 column blocks (one group's compact block, or the ends of two): not a
 //    run along one row's columns.
+// Then, for extra workgroups past a launch's tiles (xcd_range_pos), that
+// each range maps onto its positions once, in contiguous per-XCD runs.
 // Prints "ok <count>", or the first violation and exits 1.
 #include <cstdio>
 #include <set>
@@ -70,6 +72,26 @@ static int check(int nbm, int nbn, long long w_bytes) {
   return 0;
 }
 
+// Extra workgroups [lo, hi) of a launch (xcd_range_pos): positions 0 ..
+// hi-lo-1 each exactly once, and each XCD's workgroups, in dispatch order,
+// on consecutive positions, the runs following XCD order.
+static int check_range(int lo, int hi) {
+  std::vector<int> seen(size_t(hi - lo), 0);
+  for (int b = lo; b < hi; ++b) {
+    const int p = xcd_range_pos(b, lo, hi);
+    if (p < 0 || p >= hi - lo) return fail("range position outside", lo, hi, b);
+    if (seen[size_t(p)]++) return fail("range position taken twice", lo, hi, b);
+  }
+  int next = 0;
+  for (int x = 0; x < 8; ++x)
+    for (int b = lo; b < hi; ++b)
+      if ((b & 7) == x) {
+        if (xcd_range_pos(b, lo, hi) != next) return fail("range run not contiguous", lo, hi, b);
+        ++next;
+      }
+  return 0;
+}
+
 int main() {
   int nbm, nbn;
   long long w_bytes;
@@ -78,6 +100,17 @@ int main() {
     if (check(nbm, nbn, w_bytes)) return 1;
     ++count;
   }
+  const int los[] = {0, 1, 3, 7, 8, 9, 148, 228, 684};
+  for (int lo : los)
+    for (int n = 1; n <= 70; ++n) {
+      if (check_range(lo, lo + n)) return 1;
+      ++count;
+    }
+  for (int lo : los)
+    for (int n : {225, 450, 900, 1001}) {
+      if (check_range(lo, lo + n)) return 1;
+      ++count;
+    }
   std::printf("ok %d\n", count);
   return 0;
 }

@@ -809,14 +809,16 @@ def test_lowrank_proj_v_append_equals_projection_then_append(name):
     """The value projection stored straight into the ring, with the keys-only
     append, leaves the ring bit for bit as ust_lowrank_proj followed by the
     full ust_kv_append does, chunk after chunk (slots no chunk wrote and the
-    rows' padding keep the NaN fill).  On the small shape the values are also
-    compared with the fp64 oracle."""
+    rows' padding keep the NaN fill); so does the same call given the keys,
+    which rotates and appends them in the first product's launch.  On the
+    small shape the values are also compared with the fp64 oracle."""
     w = WAN_WINDOW_D64 if name == "wan_window_d64" else wl.ALL[name]
     g = _g(w)
     print(f"[lowrank_proj_v_append {name}]", flush=True)
     table = P.RopeTable(g, w.n_tab_frames, w.theta)
     ring_ref = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
     ring = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
+    ring_k = P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS)
     a, b = wl.svd_factors_bf16(w, wl.TAG_WV, w.rank)
     p = P.LowRank.from_bits(a, b)
     HD = w.n_heads * w.head_dim
@@ -831,9 +833,13 @@ def test_lowrank_proj_v_append_equals_projection_then_append(name):
         B.ust_kv_append(g, ring_ref.abi, k, v, table.cos, table.sin, w.n_tab_frames, 3 * c)
         B.ust_kv_append(g, ring.abi, k, None, table.cos, table.sin, w.n_tab_frames, 3 * c)
         B.ust_lowrank_proj_v_append(g, ring.abi, x, p.a, p.b, t, w.hidden, w.rank, 3 * c)
+        B.ust_lowrank_proj_v_append(g, ring_k.abi, x, p.a, p.b, t, w.hidden, w.rank, 3 * c,
+                                    k_new=k, cos_tab=table.cos, sin_tab=table.sin,
+                                    n_tab_frames=table.n_frames)
     torch.cuda.synchronize()
-    assert torch.equal(ring.k.view(torch.int16), ring_ref.k.view(torch.int16))
-    assert torch.equal(ring.v.view(torch.int16), ring_ref.v.view(torch.int16))
+    for r in (ring, ring_k):
+        assert torch.equal(r.k.view(torch.int16), ring_ref.k.view(torch.int16))
+        assert torch.equal(r.v.view(torch.int16), ring_ref.v.view(torch.int16))
     if name == "mid":
         c = n_chunks - 1
         ref = O.lowrank_proj(_f64(wl.activations(w, c)), _f64(a), _f64(b))
@@ -842,6 +848,42 @@ def test_lowrank_proj_v_append_equals_projection_then_append(name):
         got = np.stack([gv[O.slot_of_frame(3 * c + i, w.n_slots, w.n_sink)].transpose(1, 0, 2)
                         for i in range(3)])
         assert_close(_f64(got), ref, "values in the ring")
+
+
+@pytest.mark.parametrize("hidden", [1536, 1544])
+def test_lowrank_proj_v_append_keys_other_widths(hidden):
+    """The value projection with the keys, at an input width the pipelined
+    product takes (1536: the keys ride in its launch) and one it does not
+    (1544, not a multiple of 64: the keys get a launch of their own, then
+    the register-staged product), against the keys-only append plus the
+    projection without keys: the same ring bit for bit.  The table starts
+    at the chunk's own first frame."""
+    w = wl.MID
+    g = _g(w)
+    print(f"[lowrank_proj_v_append keys hidden {hidden}]", flush=True)
+    rs = np.random.default_rng(81)
+    rank = 64
+    HD = w.n_heads * w.head_dim
+    a = P.to_device_bf16(wl.f32_to_bf16_bits(rs.standard_normal((rank, hidden)) * hidden ** -0.5))
+    b = P.to_device_bf16(wl.f32_to_bf16_bits(rs.standard_normal((HD, rank)) * rank ** -0.5))
+    t = torch.empty((w.n_q, rank), dtype=torch.bfloat16, device="cuda")
+    rings = [P.Ring(g, w.n_slots, w.n_sink, fill_bits=NAN_BITS) for _ in range(2)]
+    table = P.RopeTable(g, 3, w.theta)
+    for c in range(4):
+        table.rebuild(3 * c)
+        x = P.to_device_bf16(wl.f32_to_bf16_bits(rs.standard_normal((w.n_q, hidden))))
+        k = P.to_device_bf16(wl.chunk_tokens(w, wl.TAG_K, c).reshape(w.n_q, -1))
+        B.ust_kv_append(g, rings[0].abi, k, None, table.cos, table.sin, 3, 3 * c,
+                        tab_first_frame=3 * c)
+        B.ust_lowrank_proj_v_append(g, rings[0].abi, x, a, b, t, hidden, rank, 3 * c)
+        B.ust_lowrank_proj_v_append(g, rings[1].abi, x, a, b, t, hidden, rank, 3 * c, k_new=k,
+                                    cos_tab=table.cos, sin_tab=table.sin, n_tab_frames=3,
+                                    tab_first_frame=3 * c)
+    torch.cuda.synchronize()
+    assert torch.equal(rings[0].k.view(torch.int16), rings[1].k.view(torch.int16))
+    assert torch.equal(rings[0].v.view(torch.int16), rings[1].v.view(torch.int16))
+    assert not torch.equal(rings[0].k.view(torch.int16)[3],
+                           torch.full_like(rings[0].k.view(torch.int16)[3], NAN_BITS))
 
 
 def test_keys_only_append_leaves_values():

@@ -329,7 +329,18 @@ def test_lowrank_proj_v_append_rejects_bad_arguments(lib):
     ring = B.Kv(fake, fake, 21, 3)
     gp, rp = ctypes.byref(g), ctypes.byref(ring)
     call = lambda x, t, hidden, rank, f0, rr=rp: _raw(lib, "ust_lowrank_proj_v_append", gp, rr, x,
-                                                     fake, fake, t, hidden, rank, f0, None)
+                                                     fake, fake, t, hidden, rank, None, None,
+                                                     None, 0, 0, f0, None)
+    # with the keys: k_new, table, table range
+    callk = lambda k, cs, t0, n_tab, f0: _raw(lib, "ust_lowrank_proj_v_append", gp, rp, fake, fake,
+                                              fake, fake, 1536, 512, k, cs, fake, t0, n_tab, f0,
+                                              None)
+    assert callk(fake, None, 0, 21, 0)[0] == "UST_E_NULL"
+    assert callk(fake + 8, fake, 0, 21, 0)[0] == "UST_E_ALIGN"
+    assert callk(fake, fake + 4, 0, 21, 0)[0] == "UST_E_ALIGN"
+    assert callk(fake, fake, 0, 21, 19)[0] == "UST_E_RANGE"        # frames 19..21
+    assert callk(fake, fake, 9, 3, 6)[0] == "UST_E_RANGE"          # chunk before the table
+    assert callk(fake, fake, -1, 21, 0)[0] == "UST_E_RANGE"
     assert call(None, fake, 1536, 512, 0)[0] == "UST_E_NULL"
     assert call(fake, None, 1536, 512, 0)[0] == "UST_E_NULL"
     assert call(fake + 8, fake, 1536, 512, 0)[0] == "UST_E_ALIGN"
@@ -434,7 +445,9 @@ def test_gemm_tile_order_covers_every_tile_once(tmp_path):
     """The pipelined GEMM's tile order (gemm_order.h, shared with the kernel),
     run on the CPU: every tile once, a contiguous run of tiles per XCD, the
     row-major order exactly when the grid fits one round or W fits one L2,
-    and compact blocks per XCD in the grouped order."""
+    and compact blocks per XCD in the grouped order; and the positions of
+    the extra (key-append) workgroups past the tiles: each once, in
+    contiguous per-XCD runs."""
     from causal_video_diffusion_amd import build
     exe = tmp_path / "gemm_order_check"
     src = os.path.join(ROOT, "tests", "gemm_order_check.cpp")
@@ -453,7 +466,9 @@ def test_gemm_tile_order_covers_every_tile_once(tmp_path):
                 cases.append((nbm, nbn, wb))
     inp = "".join(f"{m} {n} {w}\n" for m, n, w in cases)
     r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, timeout=120)
-    assert r.returncode == 0 and r.stdout.strip() == f"ok {len(cases)}", r.stdout
+    # then the extra workgroups' order: 9 range starts x (70 small + 4 large) sizes
+    n_ranges = 9 * (70 + 4)
+    assert r.returncode == 0 and r.stdout.strip() == f"ok {len(cases) + n_ranges}", r.stdout
 
 
 def test_status_strings(lib):
