@@ -850,17 +850,18 @@ def test_lowrank_proj_v_append_equals_projection_then_append(name):
         assert_close(_f64(got), ref, "values in the ring")
 
 
-@pytest.mark.parametrize("hidden", [1536, 1544])
-def test_lowrank_proj_v_append_keys_other_widths(hidden):
+@pytest.mark.parametrize("heads,hidden", [(12, 1536), (12, 1544), (3, 1536)])
+def test_lowrank_proj_v_append_keys_other_widths(heads, hidden):
     """The value projection with the keys, at an input width the pipelined
     product takes (1536: the keys ride in its launch) and one it does not
     (1544, not a multiple of 64: the keys get a launch of their own, then
     the register-staged product), against the keys-only append plus the
-    projection without keys: the same ring bit for bit.  The table starts
-    at the chunk's own first frame."""
-    w = wl.MID
+    projection without keys: the same ring bit for bit.  With 3 heads a
+    chunk has 18 key tiles, so the last key workgroup holds two (of four).
+    The table starts at the chunk's own first frame."""
+    w = wl.MID.replace(n_heads=heads)
     g = _g(w)
-    print(f"[lowrank_proj_v_append keys hidden {hidden}]", flush=True)
+    print(f"[lowrank_proj_v_append keys: {heads} heads, hidden {hidden}]", flush=True)
     rs = np.random.default_rng(81)
     rank = 64
     HD = w.n_heads * w.head_dim
