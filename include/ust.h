@@ -5,8 +5,9 @@
  * "UnStep: Training-Free Acceleration of Causal Video Diffusion with Fewer
  * Steps Than Distillation"), as a C ABI over hand-written gfx950 kernels:
  *
- *   ust_rope_table_build  cos/sin coefficients of the 3-D RoPE, cached once
- *                         (abstract: RoPE from precomputed coefficients)
+ *   ust_rope_table_build  cos/sin coefficients of the 3-D RoPE for a range of
+ *                         frames, cached (abstract: RoPE from precomputed
+ *                         coefficients); a chunk's own frames suffice
  *   ust_kv_append         RoPE the chunk's keys and store keys and values in
  *                         the frame slots of a KV ring (abstract: the KV
  *                         cache and its indexing)
@@ -23,7 +24,8 @@
  *   ust_lowrank_proj      Y = (X A_r) B_r, the truncated-SVD value and output
  *                         projections (abstract; Table 5 caption)
  *   ust_lowrank_proj_v_append  the value projection with the values stored
- *                         straight into the ring's slots
+ *                         straight into the ring's slots, and the keys' RoPE
+ *                         and append in the same call
  *   ust_lowrank_proj_static  the same with the intermediate in a fixed device
  *                         array, for callers that cannot allocate
  *   ust_flow_step         one step of the chunk sampler: denoised estimate and
