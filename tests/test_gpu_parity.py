@@ -850,18 +850,20 @@ def test_lowrank_proj_v_append_equals_projection_then_append(name):
         assert_close(_f64(got), ref, "values in the ring")
 
 
-@pytest.mark.parametrize("heads,hidden", [(12, 1536), (12, 1544), (3, 1536)])
-def test_lowrank_proj_v_append_keys_other_widths(heads, hidden):
+@pytest.mark.parametrize("base,heads,hidden", [("mid", 12, 1536), ("mid", 12, 1544),
+                                               ("mid", 3, 1536), ("mid64", 3, 192)])
+def test_lowrank_proj_v_append_keys_other_widths(base, heads, hidden):
     """The value projection with the keys, at an input width the pipelined
     product takes (1536: the keys ride in its launch) and one it does not
     (1544, not a multiple of 64: the keys get a launch of their own, then
     the register-staged product), against the keys-only append plus the
     projection without keys: the same ring bit for bit.  With 3 heads a
-    chunk has 18 key tiles, so the last key workgroup holds two (of four).
-    The table starts at the chunk's own first frame."""
-    w = wl.MID.replace(n_heads=heads)
+    chunk has 18 key tiles (9 at head size 64 and 40 tokens per frame), so
+    the last key workgroup holds two (one) of its four.  The table starts
+    at the chunk's own first frame."""
+    w = wl.ALL[base].replace(n_heads=heads)
     g = _g(w)
-    print(f"[lowrank_proj_v_append keys: {heads} heads, hidden {hidden}]", flush=True)
+    print(f"[lowrank_proj_v_append keys: {base}, {heads} heads, hidden {hidden}]", flush=True)
     rs = np.random.default_rng(81)
     rank = 64
     HD = w.n_heads * w.head_dim
