@@ -9,6 +9,9 @@
  *  - on random inputs the key-split schedule (5 workgroups) agrees with the
  *    one-workgroup-per-tile schedule within the bf16 bar, and both are finite;
  *  - ust_window_attn_work_bytes matches its stated formula;
+ *  - a RoPE table of the last chunk's own three frames gives the attention
+ *    bit for bit as the table from frame 0, and ranges it does not hold are
+ *    rejected;
  *  - ust_sigma_schedule gives the shift-5 levels 1 and 5/6 for raw 1000 and
  *    500, and ust_flow_step matches a double-precision loop within fp32
  *    rounding (2^-21 of the magnitudes involved: four roundings at most),
@@ -142,6 +145,26 @@ int main(void) {
       }
       EXPECT(max_d <= 2e-2, "split vs unsplit differ by %g (pass %d chunk %d)", max_d, pass, c);
     }
+  }
+  /* a table of the last chunk's own frames gives the same attention, bit for
+     bit, as the table from frame 0 (h1 holds that chunk's output) */
+  {
+    const int f0 = CF * (N_CHUNKS - 1);
+    float *cs3, *sn3;
+    const size_t nt3 = (size_t)CF * T * (D / 2);
+    HIP_OK(hipMalloc((void**)&cs3, nt3 * 4));
+    HIP_OK(hipMalloc((void**)&sn3, nt3 * 4));
+    EXPECT(ust_rope_table_build(&g, -1, CF, 10000.0, cs3, sn3, 0) == UST_E_RANGE,
+           "negative first frame accepted");
+    UST_OK_(ust_rope_table_build(&g, f0, CF, 10000.0, cs3, sn3, 0));
+    EXPECT(ust_window_attn(&g, &ring, q, cs3, sn3, f0 + 1, CF, f0, N_RECENT, 0.f, o2, NULL, 0) ==
+               UST_E_RANGE, "chunk before the table accepted");
+    UST_OK_(ust_window_attn(&g, &ring, q, cs3, sn3, f0, CF, f0, N_RECENT, 0.f, o2, NULL, 0));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(h2, o2, nc * 2, hipMemcpyDeviceToHost));
+    EXPECT(memcmp(h1, h2, nc * 2) == 0, "chunk table and full table differ");
+    HIP_OK(hipFree(cs3));
+    HIP_OK(hipFree(sn3));
   }
   /* the sampler step */
   {
