@@ -56,6 +56,7 @@ ATTN_TRAFFIC = {
 CONV_SOURCES = ("conv3d.hip", "ust_device.h")
 CONV_TRAFFIC = {
     "vae_conv": {"src_sha16": "a69f954fab1ff211", "bytes": (2 * 62222 + 32760) * 1024},
+    "vae_conv_in": {"src_sha16": "a69f954fab1ff211", "bytes": (2 * 3970 + 32760) * 1024},
 }
 # the sampler's flow step at the Wan chunk latent, per launch averaged over
 # one clip's 23 (16 renoising ones read the noise: FETCH 1478 KiB; 7
@@ -642,7 +643,9 @@ def main_fused(args):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            # the same attention kernel at the same shape and schedule as
+            # the windowed layer-chunk's line: its counter-measured bytes
+            "traffic": attn_traffic(w.name, schedule),
             "kernel": "window_attn_kernel<128> (per-stage pass)",
         },
         "stages_us": stage,
